@@ -1,0 +1,259 @@
+"""ctypes binding of libblockattn.so: argument marshalling only.
+
+Every function here takes torch tensors that already live on the GPU, checks
+that their shapes and strides fit the C ABI (include/blockattn.h), passes raw
+device pointers, element strides and the current HIP stream, and raises if the
+library returns an error status.  All arithmetic runs in the library's HIP
+kernels; there is no CPU fallback, and importing this module fails loudly when
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblockattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "blockattn.h")
+
+BA_OK = 0
+BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_STRIDE, BA_ERR_ALIGN = 1, 2, 3, 4
+BA_ERR_UNSUPPORTED, BA_ERR_S2, BA_ERR_MODE, BA_ERR_LAUNCH = 5, 6, 7, 8
+BA_F32, BA_BF16 = 0, 1
+BA_OVERWRITE, BA_ACCUMULATE = 0, 1
+BA_BWD_COMPUTE_DELTA, BA_BWD_FINALIZE_DQ = 1, 2
+
+
+class BaDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("seqlen_q", ctypes.c_int64),
+        ("seqlen_k", ctypes.c_int64),
+        ("q_pos0", ctypes.c_int64),
+        ("k_pos0", ctypes.c_int64),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("kv_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class BaS2Desc(ctypes.Structure):
+    _fields_ = [("group", ctypes.c_int32), ("shift_head0", ctypes.c_int32)]
+
+
+class BlockAttnError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Load libblockattn.so (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first (python -c "
+            "'import __graft_entry__; __graft_entry__.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(BaDesc)
+    S2 = ctypes.POINTER(BaS2Desc)
+    i32 = ctypes.c_int32
+    lib.blockattn_fwd.argtypes = [D, P, P, P, P, i32, P, i32, P, P]
+    lib.blockattn_fwd.restype = ctypes.c_int
+    lib.lse_merge.argtypes = [D, P, P, P, i32, P, P, P]
+    lib.lse_merge.restype = ctypes.c_int
+    lib.blockattn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
+    lib.blockattn_bwd.restype = ctypes.c_int
+    lib.s2attn_fwd.argtypes = [D, S2, P, P, P, P, i32, P, P]
+    lib.s2attn_fwd.restype = ctypes.c_int
+    lib.s2attn_bwd.argtypes = [D, S2, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
+    lib.s2attn_bwd.restype = ctypes.c_int
+    lib.blockattn_status_string.argtypes = [ctypes.c_int]
+    lib.blockattn_status_string.restype = ctypes.c_char_p
+    lib.blockattn_debug_fwd_schedule.argtypes = [D, S2, i32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
+    lib.blockattn_debug_fwd_schedule.restype = ctypes.c_int64
+    lib.blockattn_debug_tile_sizes.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.blockattn_debug_tile_sizes.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions include/blockattn.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)) - {"if"})
+
+
+def status_string(status):
+    return load().blockattn_status_string(int(status)).decode()
+
+
+def _check(status, fn):
+    if status != BA_OK:
+        raise BlockAttnError(status, fn)
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _bshd_strides(t, name):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, S, H, D]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous last (D) axis")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def _same_layout(ref, t, name, shape=None):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(ref.shape if shape is None else shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+    if t.dim() == 4 and _bshd_strides(t, name) != _bshd_strides(ref, "q"):
+        raise ValueError(f"{name} must have the same (b, s, h) strides as q")
+
+
+def _stats_ok(t, shape, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {tuple(shape)}")
+
+
+def make_desc(q, k, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
+    b, sq, hq, d = q.shape
+    sk, hkv = (k.shape[1], k.shape[2]) if k is not None else (0, hq)
+    desc = BaDesc()
+    desc.batch, desc.heads_q, desc.heads_kv, desc.head_dim = b, hq, hkv, d
+    desc.seqlen_q, desc.seqlen_k = sq, sk
+    desc.q_pos0, desc.k_pos0 = int(q_pos0), int(k_pos0)
+    desc.causal = 1 if causal else 0
+    desc.scale = 0.0 if scale is None else float(scale)
+    desc.q_stride[:] = _bshd_strides(q, "q")
+    desc.kv_stride[:] = _bshd_strides(k, "k") if k is not None else (0, 0, 0)
+    return desc
+
+
+def _dtype_code(t, name):
+    import torch
+    if t.dtype == torch.float32:
+        return BA_F32
+    if t.dtype == torch.bfloat16:
+        return BA_BF16
+    raise ValueError(f"{name} must be float32 or bfloat16")
+
+
+# ---------------------------------------------------------------- entry points
+
+def blockattn_fwd(q, k, v, o, lse, *, mode=BA_OVERWRITE, o_final=None, q_pos0=0, k_pos0=0,
+                  causal=True, scale=None, stream=None):
+    """One ring step; see blockattn_fwd in include/blockattn.h."""
+    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+    if tuple(v.shape) != tuple(k.shape) or _bshd_strides(v, "v") != _bshd_strides(k, "k"):
+        raise ValueError("v must match k in shape and strides")
+    _same_layout(q, o, "o")
+    _same_layout(q, o_final, "o_final")
+    _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
+    st = load().blockattn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _dtype_code(o, "o"), _ptr(lse), int(mode), _ptr(o_final), _stream(stream))
+    _check(st, "blockattn_fwd")
+
+
+def lse_merge(o_acc, lse_acc, o_part, lse_part, *, o_final=None, stream=None):
+    """(o_acc, lse_acc) := merge with (o_part, lse_part); see lse_merge in include/blockattn.h."""
+    desc = make_desc(o_acc, None)
+    _same_layout(o_acc, o_part, "o_part")
+    _same_layout(o_acc, o_final, "o_final")
+    shape = (o_acc.shape[0], o_acc.shape[2], o_acc.shape[1])
+    _stats_ok(lse_acc, shape, "lse_acc")
+    _stats_ok(lse_part, shape, "lse_part")
+    st = load().lse_merge(ctypes.byref(desc), _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
+                          _dtype_code(o_part, "o_part"), _ptr(lse_part), _ptr(o_final), _stream(stream))
+    _check(st, "lse_merge")
+
+
+def s2attn_fwd(q, k, v, o, lse, *, group, shift_head0, scale=None, stream=None):
+    desc = make_desc(q, k, causal=True, scale=scale)
+    _same_layout(q, o, "o")
+    _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
+    s2 = BaS2Desc(int(group), int(shift_head0))
+    st = load().s2attn_fwd(ctypes.byref(desc), ctypes.byref(s2), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                           _dtype_code(o, "o"), _ptr(lse), _stream(stream))
+    _check(st, "s2attn_fwd")
+
+
+def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None, flags=0,
+                  q_pos0=0, k_pos0=0, causal=True, scale=None, stream=None):
+    """One ring step of the backward; see blockattn_bwd in include/blockattn.h."""
+    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+    for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
+        _same_layout(q, t, n)
+    for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
+        if tuple(t.shape) != tuple(k.shape) or _bshd_strides(t, n) != _bshd_strides(k, "k"):
+            raise ValueError(f"{n} must match k in shape and strides")
+    if dk.dtype != dv.dtype:
+        raise ValueError("dk and dv must share a dtype")
+    shape = (q.shape[0], q.shape[2], q.shape[1])
+    _stats_ok(lse, shape, "lse")
+    _stats_ok(delta, shape, "delta")
+    st = load().blockattn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
+                              _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
+    _check(st, "blockattn_bwd")
+
+
+def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_head0, dq_final=None,
+               flags=0, scale=None, stream=None):
+    desc = make_desc(q, k, causal=True, scale=scale)
+    for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
+        _same_layout(q, t, n)
+    shape = (q.shape[0], q.shape[2], q.shape[1])
+    _stats_ok(lse, shape, "lse")
+    _stats_ok(delta, shape, "delta")
+    s2 = BaS2Desc(int(group), int(shift_head0))
+    st = load().s2attn_bwd(ctypes.byref(desc), ctypes.byref(s2), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                           _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
+                           _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
+    _check(st, "s2attn_bwd")
+
+
+def debug_fwd_schedule(desc, head, s2=None):
+    """Host-side enumeration of the forward tile schedule: int64 array [n, 4]."""
+    import numpy as np
+    lib = load()
+    s2p = ctypes.byref(s2) if s2 is not None else None
+    n = lib.blockattn_debug_fwd_schedule(ctypes.byref(desc), s2p, int(head), None, 0)
+    if n < 0:
+        raise BlockAttnError(-n, "blockattn_debug_fwd_schedule")
+    buf = (ctypes.c_int64 * (4 * max(n, 1)))()
+    lib.blockattn_debug_fwd_schedule(ctypes.byref(desc), s2p, int(head), buf, n)
+    return np.frombuffer(buf, dtype=np.int64, count=4 * n).reshape(n, 4).copy()
+
+
+def debug_tile_sizes(head_dim):
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().blockattn_debug_tile_sizes(int(head_dim), ctypes.byref(bq), ctypes.byref(bk)),
+           "blockattn_debug_tile_sizes")
+    return bq.value, bk.value

@@ -1,0 +1,52 @@
+// Shared device types and small helpers for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BA_HD __host__ __device__ __forceinline__
+
+namespace ba {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+
+// v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] * B[16x32].
+// Accumulator layout (measured on gfx950): lane l, register r holds
+// C[8*(r/4) + 4*(l/32) + r%4][l%32].  The k index of an operand register is
+// the same function of (l/32, item) for A and B, so any consistent k order of
+// the two operands gives the product.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Hardware base-2 exponential / logarithm (v_exp_f32, v_log_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
+// item j = the (i%4)-th 16-bit value at the address supplied by lane (i/4)+4j.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+#endif
+
+}  // namespace ba

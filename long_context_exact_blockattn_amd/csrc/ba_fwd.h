@@ -1,0 +1,281 @@
+// Forward kernel: one ring step of exact blockwise attention (or S2-Attn).
+//
+// Work item = (batch, query head, tile of BM = 128 query rows); 4 waves, each
+// owning 32 query rows.  Key/value tiles of BN = 64 rows stream through a
+// double-buffered LDS ring; scores and outputs use v_mfma_f32_32x32x16_bf16 in
+// the TRANSPOSED form, S^T = K Q^T and O^T += V^T P^T, so that one lane holds
+// the scores of ONE query row: the row max and row sum of the online softmax
+// are in-lane reductions plus a single exchange between the two lane halves.
+//
+// Online softmax (Milakov & Gimelshein's online normaliser, cited by the Ring
+// Attention summary's references): running max m and sum l per row, in base 2
+// with tau*log2(e) folded into one FMA; a fully masked row keeps m = -inf and
+// l = 0 without producing NaN.  The epilogue turns (acc, m, l) into the
+// chunk's partial pair and, in ACCUMULATE mode, merges it into the running
+// pair (O_acc, LSE_acc) in fp32 -- the order-independent combination of the
+// Ring Attention summary (Summary).
+#pragma once
+
+#include "ba_common.h"
+#include "ba_schedule.h"
+
+namespace ba {
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  void* o;          // fp32 or bf16 [B,Sq,Hq,D]
+  float* lse;       // [B,Hq,Sq]
+  bf16* o_final;    // nullable bf16 [B,Sq,Hq,D]
+  int64_t qs_b, qs_s, qs_h;  // element strides of query-shaped tensors
+  int64_t ks_b, ks_s, ks_h;  // element strides of key-shaped tensors
+  int64_t Sq, Sk, q_pos0, k_pos0;
+  int32_t B, Hq, Hkv, grp;
+  int32_t causal, accumulate, o_f32;
+  int32_t s2_group, s2_shift_head0;
+  float scale_log2;  // tau * log2(e)
+  int64_t n_qtiles;
+  int64_t n_items;
+};
+
+constexpr int kFwdBM = 128;
+constexpr int kFwdBN = 64;
+constexpr int kFwdThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int ROW = D + 8;            // padded LDS row (bf16 elements)
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPP = kFwdThreads / CPR;  // rows per load pass
+  constexpr int NPASS = BN / RPP;
+  constexpr int KK = D / 16;            // MFMA k-steps over D
+  constexpr int DB = D / 32;            // 32-wide blocks of D in the output
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * ROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;   // lane half
+  const int l32 = lane & 31;
+
+  // ---- work item
+  const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
+  const int64_t bh = pid / a.n_qtiles;
+  const int64_t w = pid % a.n_qtiles;
+  const int b = (int)(bh / a.Hq);
+  const int h = (int)(bh % a.Hq);
+  const int kvh = h / a.grp;
+  Sched sc;
+  sc.Sq = a.Sq; sc.Sk = a.Sk; sc.q_pos0 = a.q_pos0; sc.k_pos0 = a.k_pos0;
+  sc.causal = a.causal; sc.s2_group = a.s2_group;
+  sc.s2_shift = (a.s2_group > 0 && h >= a.s2_shift_head0) ? a.s2_group / 2 : 0;
+  sc.BM = BM; sc.BN = BN;
+  const QTile qt = make_qtile(sc, qtile_of_rank(sc, a.n_qtiles, w));
+  const bool empty = qt.kt_end <= qt.kt_begin;
+  if (empty && a.accumulate && a.o_final == nullptr) return;
+
+  const int rloc = wave * 32 + l32;            // row within the tile
+  const bool row_ok = rloc < qt.rows;
+  const int64_t row = qt.row0 + rloc;          // original query row
+  const int64_t qcpos = qt.cpos0 + rloc;       // coordinate position of this lane's row
+  const int64_t wave_cmin = qt.cpos0 + wave * 32;
+  const int64_t wave_cmax = wave_cmin + 31;
+
+  const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+  const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+
+  if (!empty) {
+    // ---- resident query fragments: B operand of S^T = K Q^T
+    bf16x8 qf[KK];
+    {
+      const bf16* qp = a.q + (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 8 * hl;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qf[kk] = row_ok ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
+    }
+
+    // Next-tile staging through registers: K is fetched at the top of an
+    // iteration and written to the free LDS buffer after the score MFMAs; V is
+    // fetched then and written after the output MFMAs.
+    u32x4 st[NPASS];
+    auto gload = [&](const bf16* base, int64_t kt) {
+      const KTile t = make_ktile(sc, kt);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = p * RPP + tid / CPR;
+        const int c = tid % CPR;
+        st[p] = r < t.rows ? *(const u32x4*)(base + (t.row0 + r) * a.ks_s + 8 * c) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto lstore = [&](bf16* dst) {
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = p * RPP + tid / CPR;
+        const int c = tid % CPR;
+        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[p];
+      }
+    };
+
+    gload(kbase, qt.kt_begin);
+    lstore(smem[0][0]);
+    gload(vbase, qt.kt_begin);
+    lstore(smem[0][1]);
+    __syncthreads();
+
+    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; ++kt) {
+      const int buf = (int)((kt - qt.kt_begin) & 1);
+      const bool has_next = kt + 1 < qt.kt_end;
+      if (has_next) gload(kbase, kt + 1);
+
+      const KTile t = make_ktile(sc, kt);
+      const bool wave_active = !(a.causal && t.cpos0 > wave_cmax);
+      if (wave_active) {
+        const bf16* Ks = smem[buf][0];
+        const bf16* Vs = smem[buf][1];
+        // ---- S^T = K Q^T  (two 32-key blocks)
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 kf = *(const bf16x8*)(&Ks[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
+            s[kb] = mfma32(kf, qf[kk], s[kb]);
+          }
+        }
+        if (has_next) {
+          lstore(smem[buf ^ 1][0]);
+          gload(vbase, kt + 1);
+        }
+        // ---- mask: ragged chunk tail, causal diagonal (coordinate positions)
+        const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+              const bool ok = key < t.rows && (!a.causal || t.cpos0 + key <= qcpos);
+              s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            }
+        }
+        // ---- online softmax (base 2)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx * a.scale_log2);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_hw(m_run - m_use);
+        float rsum = 0.f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -m_use));
+            rsum += p;
+            pf[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+          }
+        l_run = l_run * alpha + rsum;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+        }
+        // ---- O^T += V^T P^T ; V^T operand read transposed from the natural [key][d] tile
+        const int gi = lane & 15;
+        const int dsub = 16 * ((lane >> 4) & 1);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            const int k0 = 16 * kc + 4 * hl + (gi >> 2);
+            const int dcol = 32 * db + dsub + 4 * (gi & 3);
+            const bf16x4 v0 = lds_read_tr16(&Vs[k0 * ROW + dcol]);
+            const bf16x4 v1 = lds_read_tr16(&Vs[(k0 + 8) * ROW + dcol]);
+            const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = mfma32(vf, pf[kc], oacc[db]);
+          }
+        }
+      } else if (has_next) {
+        lstore(smem[buf ^ 1][0]);
+        gload(vbase, kt + 1);
+      }
+      if (has_next) lstore(smem[buf ^ 1][1]);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: partial pair of this chunk, optional merge into the running pair
+  const float l_tot = l_run + wave_xor32(l_run);
+  const bool has = l_tot > 0.f;
+  const float lse2_c = has ? m_run + log2_hw(l_tot) : -INFINITY;
+  const float inv_l = has ? 1.f / l_tot : 0.f;
+  if (!row_ok) return;
+
+  const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
+  const int64_t obase = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 4 * hl;
+  float ca = 0.f, cc = inv_l, L2 = lse2_c;
+  if (a.accumulate) {
+    const float la2 = a.lse[lse_idx] * kLog2e;
+    const float M = fmaxf(la2, lse2_c);
+    if (M == -INFINITY) {
+      ca = 0.f; cc = 0.f; L2 = -INFINITY;
+    } else {
+      const float wa = exp2_hw(la2 - M);
+      const float wc = exp2_hw(lse2_c - M);
+      const float tot = wa + wc;
+      L2 = M + log2_hw(tot);
+      ca = wa / tot;
+      cc = wc / tot * inv_l;
+    }
+  }
+  const bool write_state = !(a.accumulate && empty);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t off = obase + 32 * db + 8 * g;
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = cc * oacc[db][4 * g + e];
+      if (a.accumulate && ca > 0.f) {
+        const f32x4 prev = *(const f32x4*)((const float*)a.o + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(ca, prev[e], val[e]);
+      }
+      if (write_state) {
+        if (a.o_f32) {
+          *(f32x4*)((float*)a.o + off) = val;
+        } else {
+          bf16x4 bv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
+          *(bf16x4*)((bf16*)a.o + off) = bv;
+        }
+      }
+      if (a.o_final) {
+        bf16x4 bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
+        *(bf16x4*)(a.o_final + off) = bv;
+      }
+    }
+  }
+  if (write_state && hl == 0) a.lse[lse_idx] = L2 * kLn2;
+#endif
+}
+
+}  // namespace ba

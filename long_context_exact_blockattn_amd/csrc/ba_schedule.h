@@ -1,0 +1,112 @@
+// Tile scheduler: integer index math shared by host and device.
+//
+// A work item is one (batch, query head, query tile).  For each item the
+// scheduler gives the query rows it owns and the range of key tiles it must
+// visit, already clipped to what the mask can allow:
+//   - causal: keys at global positions <= the last query position of the tile
+//     (Ring Attention summary, Summary: a host's query block against one
+//     key/value block per step, chunk offset k_pos0 = global position);
+//   - S2-Attn: keys of the same group of rolled positions, up to the tile's
+//     last rolled position (LongLoRA summary, Summary: groups, half of the heads
+//     shifted by half a group).  Rolled position r of a shifted head is original
+//     row (r + G/2) mod S; tiles never straddle the wrap because the tile sizes
+//     divide G/2, so every tile is one contiguous run of original rows.
+// Masks are evaluated in "coordinate positions": global positions for plain
+// causal attention, rolled positions for S2.
+#pragma once
+
+#include "ba_common.h"
+
+namespace ba {
+
+struct Sched {
+  int64_t Sq, Sk, q_pos0, k_pos0;
+  int32_t causal;
+  int32_t s2_group;  // 0: no S2
+  int32_t s2_shift;  // rows of roll for this head (0 or group/2)
+  int32_t BM, BN;
+};
+
+struct QTile {
+  int64_t row0;      // original row of the tile's first query
+  int64_t rows;      // valid query rows in the tile (<= BM)
+  int64_t cpos0;     // coordinate position of the first query
+  int64_t kt_begin;  // first key tile to visit
+  int64_t kt_end;    // one past the last key tile to visit
+};
+
+struct KTile {
+  int64_t row0;   // original row (into the key chunk) of the first key
+  int64_t rows;   // valid keys in the tile (<= BN)
+  int64_t cpos0;  // coordinate position of the first key
+};
+
+BA_HD int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+BA_HD int64_t num_qtiles(const Sched& s) { return ceil_div(s.Sq, s.BM); }
+
+BA_HD QTile make_qtile(const Sched& s, int64_t qt) {
+  QTile t;
+  if (s.s2_group > 0) {
+    const int64_t r0 = qt * s.BM;  // rolled position of the first query
+    t.row0 = (r0 + s.s2_shift) % s.Sq;
+    t.rows = s.BM;
+    t.cpos0 = r0;
+    const int64_t g0 = (r0 / s.s2_group) * s.s2_group;
+    t.kt_begin = g0 / s.BN;
+    t.kt_end = ceil_div(r0 + s.BM, s.BN);
+    return t;
+  }
+  t.row0 = qt * s.BM;
+  t.rows = s.Sq - t.row0 < s.BM ? s.Sq - t.row0 : s.BM;
+  t.cpos0 = s.q_pos0 + t.row0;
+  t.kt_begin = 0;
+  const int64_t nkt = ceil_div(s.Sk, s.BN);
+  if (!s.causal) {
+    t.kt_end = nkt;
+  } else {
+    // last key index j with k_pos0 + j <= q_pos0 + row0 + rows - 1
+    const int64_t last = s.q_pos0 + t.row0 + t.rows - 1 - s.k_pos0;
+    t.kt_end = last < 0 ? 0 : (last / s.BN + 1 < nkt ? last / s.BN + 1 : nkt);
+  }
+  return t;
+}
+
+BA_HD KTile make_ktile(const Sched& s, int64_t kt) {
+  KTile k;
+  if (s.s2_group > 0) {
+    const int64_t r0 = kt * s.BN;
+    k.row0 = (r0 + s.s2_shift) % s.Sk;
+    k.rows = s.BN;
+    k.cpos0 = r0;
+    return k;
+  }
+  k.row0 = kt * s.BN;
+  k.rows = s.Sk - k.row0 < s.BN ? s.Sk - k.row0 : s.BN;
+  k.cpos0 = s.k_pos0 + k.row0;
+  return k;
+}
+
+// Visiting order inside one (batch, head): the w-th item is the query tile with
+// the most work first, so that the grid drains with the lightest tiles last.
+BA_HD int64_t qtile_of_rank(const Sched& s, int64_t nq, int64_t w) {
+  if (s.s2_group > 0) {
+    const int64_t per_group = s.s2_group / s.BM;
+    const int64_t ngroups = nq / per_group;
+    const int64_t pos = per_group - 1 - w / ngroups;
+    const int64_t g = w % ngroups;
+    return g * per_group + pos;
+  }
+  return nq - 1 - w;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  The
+// remap gives XCD x the contiguous logical range [x*per, (x+1)*per), so the
+// query tiles of one head (which read the same keys and values) share one L2.
+BA_HD int64_t xcd_remap(int64_t pid, int64_t n) {
+  const int64_t per = n / 8;
+  const int64_t full = per * 8;
+  return pid < full ? (pid % 8) * per + pid / 8 : pid;
+}
+
+}  // namespace ba

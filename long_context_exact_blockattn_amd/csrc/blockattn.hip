@@ -1,0 +1,207 @@
+// C ABI of the blockwise attention library: validation, dispatch, launches.
+// Declarations and the contract of every entry point are in include/blockattn.h.
+#include "../../include/blockattn.h"
+
+#include <math.h>
+
+#include "ba_bwd.h"
+#include "ba_common.h"
+#include "ba_fwd.h"
+#include "ba_merge.h"
+#include "ba_schedule.h"
+
+namespace {
+
+using namespace ba;
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int check_strides(const int64_t s[3]) {
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || s[i] % 8 != 0) return BA_ERR_STRIDE;
+  return BA_OK;
+}
+
+// Shape/stride checks common to every entry point.
+int check_desc(const ba_desc* d) {
+  if (!d) return BA_ERR_NULL;
+  if (d->batch < 0 || d->heads_q < 1 || d->heads_kv < 1 || d->seqlen_q < 0 || d->seqlen_k < 0)
+    return BA_ERR_SHAPE;
+  if (d->heads_q % d->heads_kv != 0) return BA_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return BA_ERR_UNSUPPORTED;
+  if (d->causal != 0 && d->causal != 1) return BA_ERR_SHAPE;
+  int r = check_strides(d->q_stride);
+  if (r) return r;
+  return check_strides(d->kv_stride);
+}
+
+int check_s2(const ba_desc* d, const ba_s2_desc* s2) {
+  if (!s2) return BA_ERR_NULL;
+  if (d->seqlen_q != d->seqlen_k || d->q_pos0 != 0 || d->k_pos0 != 0 || d->causal != 1)
+    return BA_ERR_S2;
+  if (s2->group <= 0 || s2->group % 2 != 0) return BA_ERR_S2;
+  if (d->seqlen_q % s2->group != 0) return BA_ERR_S2;
+  if ((s2->group / 2) % kFwdBM != 0) return BA_ERR_S2;
+  const int grp = d->heads_q / d->heads_kv;
+  if (s2->shift_head0 < 0 || s2->shift_head0 > d->heads_q || s2->shift_head0 % grp != 0)
+    return BA_ERR_S2;
+  return BA_OK;
+}
+
+float scale_of(const ba_desc* d) {
+  return d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->head_dim));
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? BA_OK : BA_ERR_LAUNCH; }
+
+Sched sched_of(const ba_desc* d, const ba_s2_desc* s2, int head) {
+  Sched s;
+  s.Sq = d->seqlen_q; s.Sk = d->seqlen_k; s.q_pos0 = d->q_pos0; s.k_pos0 = d->k_pos0;
+  s.causal = s2 ? 1 : d->causal;
+  s.s2_group = s2 ? s2->group : 0;
+  s.s2_shift = (s2 && head >= s2->shift_head0) ? s2->group / 2 : 0;
+  s.BM = kFwdBM; s.BN = kFwdBN;
+  return s;
+}
+
+int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* k, const void* v,
+             void* o, int32_t o_dtype, float* lse, int32_t mode, void* o_final, hipStream_t stream) {
+  int r = check_desc(d);
+  if (r) return r;
+  if (s2 && (r = check_s2(d, s2))) return r;
+  if (mode != BA_OVERWRITE && mode != BA_ACCUMULATE) return BA_ERR_MODE;
+  if (o_dtype != BA_F32 && o_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;
+  if (mode == BA_ACCUMULATE && o_dtype != BA_F32) return BA_ERR_MODE;
+  if (d->batch == 0 || d->seqlen_q == 0) return BA_OK;
+  if (!q || !o || !lse) return BA_ERR_NULL;
+  if (d->seqlen_k > 0 && (!k || !v)) return BA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4) || !aligned(o_final, 16) ||
+      !aligned(k, 16) || !aligned(v, 16))
+    return BA_ERR_ALIGN;
+
+  FwdArgs a;
+  a.q = (const bf16*)q; a.k = (const bf16*)k; a.v = (const bf16*)v;
+  a.o = o; a.lse = lse; a.o_final = (bf16*)o_final;
+  a.qs_b = d->q_stride[0]; a.qs_s = d->q_stride[1]; a.qs_h = d->q_stride[2];
+  a.ks_b = d->kv_stride[0]; a.ks_s = d->kv_stride[1]; a.ks_h = d->kv_stride[2];
+  a.Sq = d->seqlen_q; a.Sk = d->seqlen_k; a.q_pos0 = d->q_pos0; a.k_pos0 = d->k_pos0;
+  a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.grp = d->heads_q / d->heads_kv;
+  a.causal = s2 ? 1 : d->causal;
+  a.accumulate = mode == BA_ACCUMULATE;
+  a.o_f32 = o_dtype == BA_F32;
+  a.s2_group = s2 ? s2->group : 0;
+  a.s2_shift_head0 = s2 ? s2->shift_head0 : 0;
+  a.scale_log2 = scale_of(d) * kLog2e;
+  a.n_qtiles = ceil_div(d->seqlen_q, kFwdBM);
+  a.n_items = (int64_t)d->batch * d->heads_q * a.n_qtiles;
+  if (a.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
+  const dim3 grid((unsigned)a.n_items), block(kFwdThreads);
+  if (d->head_dim == 128)
+    hipLaunchKernelGGL(fwd_kernel<128>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<64>, grid, block, 0, stream, a);
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+int blockattn_fwd(const ba_desc* desc, const void* q, const void* k, const void* v, void* o,
+                  int32_t o_dtype, float* lse, int32_t mode, void* o_final, hipStream_t stream) {
+  return fwd_impl(desc, nullptr, q, k, v, o, o_dtype, lse, mode, o_final, stream);
+}
+
+int s2attn_fwd(const ba_desc* desc, const ba_s2_desc* s2, const void* q, const void* k,
+               const void* v, void* o, int32_t o_dtype, float* lse, hipStream_t stream) {
+  if (!desc) return BA_ERR_NULL;
+  if (!s2) return BA_ERR_NULL;
+  return fwd_impl(desc, s2, q, k, v, o, o_dtype, lse, BA_OVERWRITE, nullptr, stream);
+}
+
+int lse_merge(const ba_desc* d, float* o_acc, float* lse_acc, const void* o_part,
+              int32_t part_dtype, const float* lse_part, void* o_final, hipStream_t stream) {
+  int r = check_desc(d);
+  if (r) return r;
+  if (part_dtype != BA_F32 && part_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;
+  if (d->batch == 0 || d->seqlen_q == 0) return BA_OK;
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return BA_ERR_NULL;
+  if (!aligned(o_acc, 16) || !aligned(o_part, 16) || !aligned(o_final, 16) ||
+      !aligned(lse_acc, 4) || !aligned(lse_part, 4))
+    return BA_ERR_ALIGN;
+  MergeArgs a;
+  a.o_acc = o_acc; a.lse_acc = lse_acc; a.o_part = o_part; a.lse_part = lse_part;
+  a.o_final = (bf16*)o_final;
+  a.s_b = d->q_stride[0]; a.s_s = d->q_stride[1]; a.s_h = d->q_stride[2];
+  a.Sq = d->seqlen_q; a.Hq = d->heads_q; a.D = d->head_dim; a.part_f32 = part_dtype == BA_F32;
+  a.n_threads = (int64_t)d->batch * d->seqlen_q * d->heads_q * (d->head_dim / 8);
+  const int64_t blocks = ceil_div(a.n_threads, 256);
+  if (blocks > 0x7fffffffLL) return BA_ERR_SHAPE;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return launched();
+}
+
+int blockattn_bwd(const ba_desc* desc, const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, float* delta, float* dq_acc, void* dk,
+                  void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags, hipStream_t stream) {
+  if (!desc) return BA_ERR_NULL;
+  return bwd_impl(desc, nullptr, q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dkv_dtype, dq_final,
+                  flags, stream);
+}
+
+int s2attn_bwd(const ba_desc* desc, const ba_s2_desc* s2, const void* q, const void* k,
+               const void* v, const void* o, const void* dout, const float* lse, float* delta,
+               float* dq_acc, void* dk, void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags,
+               hipStream_t stream) {
+  if (!desc || !s2) return BA_ERR_NULL;
+  return bwd_impl(desc, s2, q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dkv_dtype, dq_final,
+                  flags, stream);
+}
+
+const char* blockattn_status_string(int status) {
+  switch (status) {
+    case BA_OK: return "BA_OK";
+    case BA_ERR_NULL: return "BA_ERR_NULL: a required pointer is NULL";
+    case BA_ERR_SHAPE: return "BA_ERR_SHAPE: invalid sizes";
+    case BA_ERR_STRIDE: return "BA_ERR_STRIDE: strides must be non-negative multiples of 8 elements";
+    case BA_ERR_ALIGN: return "BA_ERR_ALIGN: tensors must be 16-byte aligned (lse/delta 4-byte)";
+    case BA_ERR_UNSUPPORTED: return "BA_ERR_UNSUPPORTED: head_dim must be 64 or 128; dtype must be F32 or BF16";
+    case BA_ERR_S2: return "BA_ERR_S2: invalid S2 layout";
+    case BA_ERR_MODE: return "BA_ERR_MODE: invalid mode/flags (ACCUMULATE needs an fp32 o)";
+    case BA_ERR_LAUNCH: return "BA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    default: return "unknown blockattn status";
+  }
+}
+
+int64_t blockattn_debug_fwd_schedule(const ba_desc* desc, const ba_s2_desc* s2, int32_t head,
+                                     int64_t* out, int64_t cap) {
+  int r = check_desc(desc);
+  if (r) return -r;
+  if (s2 && (r = check_s2(desc, s2))) return -r;
+  if (head < 0 || head >= desc->heads_q) return -BA_ERR_SHAPE;
+  const Sched s = sched_of(desc, s2, head);
+  const int64_t nq = num_qtiles(s);
+  int64_t n = 0;
+  for (int64_t w = 0; w < nq; ++w) {
+    const QTile t = make_qtile(s, qtile_of_rank(s, nq, w));
+    for (int64_t kt = t.kt_begin; kt < t.kt_end; ++kt) {
+      const KTile kt_ = make_ktile(s, kt);
+      if (out && n < cap) {
+        out[4 * n + 0] = t.row0; out[4 * n + 1] = t.rows;
+        out[4 * n + 2] = kt_.row0; out[4 * n + 3] = kt_.rows;
+      }
+      ++n;
+    }
+  }
+  return n;
+}
+
+int blockattn_debug_tile_sizes(int32_t head_dim, int32_t* block_q, int32_t* block_k) {
+  if (head_dim != 64 && head_dim != 128) return BA_ERR_UNSUPPORTED;
+  if (!block_q || !block_k) return BA_ERR_NULL;
+  *block_q = kFwdBM;
+  *block_k = kFwdBN;
+  return BA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+"""Ring steps on one GPU: the resident query block against key/value chunks in a given order.
+
+On a ring of hosts (Ring Attention summary, Summary) each host keeps its query
+block while key/value blocks arrive one per step; here the chunks are visited
+sequentially on one device, in any order, and every step is one library call
+that merges its partial (O, LSE) pair into the running pair.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _bounds(seqlen_k, n_chunks):
+    c = -(-seqlen_k // n_chunks)
+    return [(i * c, min((i + 1) * c, seqlen_k)) for i in range(n_chunks) if i * c < seqlen_k]
+
+
+def ring_forward(q, k, v, n_chunks, order=None, *, causal=True, scale=None, o_acc=None, lse=None,
+                 out=None, stream=None):
+    """Forward over `n_chunks` key/value chunks visited in `order`.
+
+    Returns (out bf16 [B,S,Hq,D], lse fp32 [B,Hq,S], o_acc fp32 [B,S,Hq,D]).
+    Step 0 overwrites the running pair (rows its chunk cannot reach become the
+    empty pair (0, -inf)); later steps accumulate; the last one also stores the
+    final bf16 output for every row.
+    """
+    bounds = _bounds(k.shape[1], n_chunks)
+    order = list(range(len(bounds))) if order is None else list(order)
+    if sorted(order) != list(range(len(bounds))):
+        raise ValueError("order must be a permutation of the chunk indices")
+    b, s, hq, d = q.shape
+    if o_acc is None:
+        o_acc = torch.empty(b, s, hq, d, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
+    if out is None:
+        out = torch.empty(b, s, hq, d, device=q.device, dtype=torch.bfloat16)
+    for t, c in enumerate(order):
+        c0, c1 = bounds[c]
+        _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
+                           mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
+                           o_final=out if t == len(order) - 1 else None,
+                           k_pos0=c0, causal=causal, scale=scale, stream=stream)
+    return out, lse, o_acc
+
+
+def ring_backward(q, k, v, o, dout, lse, n_chunks, order=None, *, causal=True, scale=None,
+                  dkv_dtype=torch.bfloat16, stream=None):
+    """Backward over key/value chunks: returns (dq bf16, dk, dv).
+
+    The first step also computes delta = rowsum(dout * o); every step writes
+    its chunk's dK, dV and adds into the fp32 dQ accumulator; the last step
+    converts dQ to bf16.
+    """
+    bounds = _bounds(k.shape[1], n_chunks)
+    order = list(range(len(bounds))) if order is None else list(order)
+    b, s, hq, d = q.shape
+    delta = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
+    dq_acc = torch.zeros(b, s, hq, d, device=q.device, dtype=torch.float32)
+    dq = torch.empty(b, s, hq, d, device=q.device, dtype=torch.bfloat16)
+    dk = torch.empty(k.shape, device=k.device, dtype=dkv_dtype)
+    dv = torch.empty(v.shape, device=v.device, dtype=dkv_dtype)
+    for t, c in enumerate(order):
+        c0, c1 = bounds[c]
+        flags = 0
+        if t == 0:
+            flags |= _lib.BA_BWD_COMPUTE_DELTA
+        if t == len(order) - 1:
+            flags |= _lib.BA_BWD_FINALIZE_DQ
+        _lib.blockattn_bwd(q, k[:, c0:c1], v[:, c0:c1], o, dout, lse, delta, dq_acc,
+                           dk[:, c0:c1], dv[:, c0:c1], dq_final=dq, flags=flags, k_pos0=c0,
+                           causal=causal, scale=scale, stream=stream)
+    return dq, dk, dv

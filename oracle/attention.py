@@ -114,18 +114,17 @@ def rows_forward(q, k, v, b: int, h: int, rows: Sequence[int], *, scale=None, ca
 
     Used to check single outputs of runs too large for the whole oracle.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
     _, _, hq, d = q.shape
     hkv = k.shape[2]
     tau = default_scale(d) if scale is None else float(scale)
     kvh = _kv_head(h, hq, hkv)
     rows = np.asarray(rows, dtype=np.int64)
-    K = k[b, :, kvh, :]
-    V = v[b, :, kvh, :]
+    # slice first, then upcast: only the rows and the one key/value head are needed
+    Q = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    K = np.asarray(k[b, :, kvh, :], dtype=np.float64)
+    V = np.asarray(v[b, :, kvh, :], dtype=np.float64)
     k_pos = k_pos0 + np.arange(K.shape[0])
-    s = tau * (q[b, rows, h, :] @ K.T)
+    s = tau * (Q @ K.T)
     p, lse = _softmax_rows(s, allowed_mask(q_pos0 + rows, k_pos, causal=causal, s2=s2, head=h))
     return p @ V, lse
 

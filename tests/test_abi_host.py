@@ -1,0 +1,166 @@
+"""Host-side tests of the C ABI: loading, exported symbols, validation, tile schedule.
+
+No kernel runs here: every call either fails validation (so nothing is
+enqueued) or is a host-only introspection entry point.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+from long_context_exact_blockattn_amd import _lib
+from oracle import S2Spec, allowed_mask
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _lib.header_functions()
+    assert {"blockattn_fwd", "blockattn_bwd", "lse_merge", "s2attn_fwd", "s2attn_bwd",
+            "blockattn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(0, 9):
+        s = _lib.status_string(code)
+        assert s.startswith("BA_"), s
+    assert "unknown" in _lib.status_string(99)
+
+
+def _desc(**kw):
+    d = _lib.BaDesc()
+    d.batch, d.heads_q, d.heads_kv, d.head_dim = kw.get("B", 1), kw.get("Hq", 2), kw.get("Hkv", 2), kw.get("D", 128)
+    d.seqlen_q, d.seqlen_k = kw.get("Sq", 256), kw.get("Sk", 256)
+    d.q_pos0, d.k_pos0 = kw.get("q0", 0), kw.get("k0", 0)
+    d.causal, d.scale = kw.get("causal", 1), 0.0
+    hq, hkv, D = d.heads_q, d.heads_kv, d.head_dim
+    d.q_stride[:] = kw.get("qs", (d.seqlen_q * hq * D, hq * D, D))
+    d.kv_stride[:] = kw.get("ks", (d.seqlen_k * hkv * D, hkv * D, D))
+    return d
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, odt=_lib.BA_F32, lse=FAKE, mode=0, of=None):
+    P = ctypes.c_void_p
+    return lib.blockattn_fwd(ctypes.byref(d) if d is not None else None, P(q), P(k), P(v), P(o), odt,
+                             P(lse), mode, P(of) if of else None, None)
+
+
+def test_fwd_validation_codes(lib):
+    assert _fwd(lib, None) == _lib.BA_ERR_NULL
+    assert _fwd(lib, _desc(D=96)) == _lib.BA_ERR_UNSUPPORTED
+    assert _fwd(lib, _desc(Hq=3, Hkv=2)) == _lib.BA_ERR_SHAPE
+    assert _fwd(lib, _desc(Sq=-1)) == _lib.BA_ERR_SHAPE
+    assert _fwd(lib, _desc(qs=(0, 12, 4))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(ks=(0, -8, 8))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(), q=FAKE + 2) == _lib.BA_ERR_ALIGN
+    assert _fwd(lib, _desc(), lse=FAKE + 2) == _lib.BA_ERR_ALIGN
+    assert _fwd(lib, _desc(), of=FAKE + 8) == _lib.BA_ERR_ALIGN
+    assert _fwd(lib, _desc(), q=0) == _lib.BA_ERR_NULL
+    assert _fwd(lib, _desc(), mode=5) == _lib.BA_ERR_MODE
+    assert _fwd(lib, _desc(), odt=_lib.BA_BF16, mode=_lib.BA_ACCUMULATE) == _lib.BA_ERR_MODE
+    assert _fwd(lib, _desc(), odt=7) == _lib.BA_ERR_UNSUPPORTED
+    assert _fwd(lib, _desc(causal=2)) == _lib.BA_ERR_SHAPE
+
+
+def test_zero_size_returns_ok_without_launch(lib):
+    # nothing is enqueued (there is no GPU here: a launch would report BA_ERR_LAUNCH)
+    assert _fwd(lib, _desc(B=0), q=0, k=0, v=0, o=0, lse=0) == _lib.BA_OK
+    assert _fwd(lib, _desc(Sq=0), q=0, k=0, v=0, o=0, lse=0) == _lib.BA_OK
+
+
+def test_merge_and_s2_validation(lib):
+    P = ctypes.c_void_p
+    d = _desc()
+    assert lib.lse_merge(ctypes.byref(d), P(FAKE), P(FAKE), P(FAKE), 3, P(FAKE), None, None) == _lib.BA_ERR_UNSUPPORTED
+    assert lib.lse_merge(ctypes.byref(d), P(FAKE), P(FAKE + 4), P(FAKE + 4), 0, P(FAKE), None, None) == _lib.BA_ERR_ALIGN
+    assert lib.lse_merge(ctypes.byref(d), None, P(FAKE), P(FAKE), 0, P(FAKE), None, None) == _lib.BA_ERR_NULL
+
+    def s2(desc, g, h0):
+        s = _lib.BaS2Desc(g, h0)
+        return lib.s2attn_fwd(ctypes.byref(desc), ctypes.byref(s), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0,
+                              P(FAKE), None)
+    assert lib.s2attn_fwd(ctypes.byref(d), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0, P(FAKE), None) == _lib.BA_ERR_NULL
+    assert s2(_desc(Sq=1024, Sk=1024), 300, 1) == _lib.BA_ERR_S2       # group does not divide S
+    assert s2(_desc(Sq=1024, Sk=1024), 128, 1) == _lib.BA_ERR_S2       # group/2 not a tile multiple
+    assert s2(_desc(Sq=1024, Sk=512), 256, 1) == _lib.BA_ERR_S2        # Sq != Sk
+    assert s2(_desc(Sq=1024, Sk=1024, k0=256), 256, 1) == _lib.BA_ERR_S2
+    assert s2(_desc(Sq=1024, Sk=1024, Hq=8, Hkv=2), 256, 3) == _lib.BA_ERR_S2  # shift boundary inside a KV group
+    assert s2(_desc(Sq=1024, Sk=1024), 256, 3) == _lib.BA_ERR_S2        # shift_head0 > Hq
+
+
+def test_bwd_validation(lib):
+    P = ctypes.c_void_p
+    d = _desc(D=80)
+    args = [P(FAKE)] * 10
+    assert lib.blockattn_bwd(ctypes.byref(d), *args, 0, None, 0, None) == _lib.BA_ERR_UNSUPPORTED
+    assert lib.blockattn_bwd(None, *args, 0, None, 0, None) == _lib.BA_ERR_NULL
+
+
+# ---------------------------------------------------------------- tile schedule
+
+def _covered_pairs(records, sq, sk):
+    """Count how many times the schedule visits each (query row, key row) pair."""
+    cnt = np.zeros((sq, sk), dtype=np.int64)
+    for q0, qn, k0, kn in records:
+        cnt[q0:q0 + qn, k0:k0 + kn] += 1
+    return cnt
+
+
+@pytest.mark.parametrize("kw", [
+    dict(Sq=1000, Sk=1000),                      # ragged causal
+    dict(Sq=512, Sk=256, k0=128),                # one ring chunk in the middle
+    dict(Sq=512, Sk=100, k0=400),                # ragged last chunk
+    dict(Sq=256, Sk=256, k0=512),                # chunk after every query: no work
+    dict(Sq=300, Sk=200, q0=50, k0=0),           # query block offset
+    dict(Sq=200, Sk=130, causal=0),              # non-causal
+    dict(Sq=256, Sk=256, D=64),
+])
+def test_schedule_covers_allowed_pairs_once(lib, kw):
+    d = _desc(**kw)
+    rec = _lib.debug_fwd_schedule(d, head=0)
+    cnt = _covered_pairs(rec, d.seqlen_q, d.seqlen_k)
+    allowed = allowed_mask(d.q_pos0 + np.arange(d.seqlen_q), d.k_pos0 + np.arange(d.seqlen_k),
+                           causal=bool(d.causal))
+    assert cnt.max() <= 1, "a (query, key) pair is visited twice"
+    assert np.all(cnt[allowed] == 1), "an allowed pair is never visited"
+    # visited but disallowed pairs only occur inside diagonal tiles (masked in the kernel)
+    bm, bn = _lib.debug_tile_sizes(d.head_dim)
+    waste = cnt[~allowed].sum()
+    assert waste <= d.seqlen_q * (bn + bm)
+
+
+@pytest.mark.parametrize("shift_head0,head", [(2, 0), (2, 3), (0, 1)])
+def test_schedule_s2(lib, shift_head0, head):
+    S, G = 2048, 512
+    d = _desc(Sq=S, Sk=S, Hq=4, Hkv=4)
+    s2 = _lib.BaS2Desc(G, shift_head0)
+    rec = _lib.debug_fwd_schedule(d, head=head, s2=s2)
+    cnt = _covered_pairs(rec, S, S)
+    allowed = allowed_mask(np.arange(S), np.arange(S), s2=S2Spec(G, shift_head0, S), head=head)
+    assert cnt.max() <= 1
+    assert np.all(cnt[allowed] == 1)
+    # every visited pair lies in the same S2 group (cross-group pairs are never visited)
+    same_group = allowed_mask(np.arange(S), np.arange(S), s2=S2Spec(G, shift_head0, S), head=head) | \
+        allowed_mask(np.arange(S), np.arange(S), s2=S2Spec(G, shift_head0, S), head=head).T
+    assert np.all(same_group[cnt > 0])
+
+
+def test_schedule_longest_first(lib):
+    d = _desc(Sq=1024, Sk=1024)
+    rec = _lib.debug_fwd_schedule(d, head=0)
+    # records come grouped by query tile in visiting order; tile work must not increase
+    tiles = []
+    for r in rec:
+        if not tiles or tiles[-1][0] != r[0]:
+            tiles.append([r[0], 0])
+        tiles[-1][1] += 1
+    work = [t[1] for t in tiles]
+    assert work == sorted(work, reverse=True)

@@ -1,0 +1,239 @@
+"""GPU parity of the forward ring step, the standalone merge and S2 forward against the oracle.
+
+Every test calls the HIP library through the C ABI (the ctypes binding) and
+compares with oracle/ on the same seeded bf16 inputs.  Gate: max|O - O_ref| <=
+1e-2 on the fp32 output the kernel computes, max|LSE - LSE_ref| <= 1e-3; the bf16
+output must equal round-to-nearest-even of the fp32 one, and its own max error
+is printed.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_blockattn_amd as ba
+from oracle import S2Spec, attention_forward, lse_merge, ring_attention_forward, rows_forward
+from tests.gpu_helpers import TOL_LSE, TOL_O, dev, f64, log, max_err, rne_bf16
+from workloads import chunk_order, get, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(*ts):
+    return [t.to(dev()) for t in ts]
+
+
+def _check_pair(tag, o32, lse, o_ref, l_ref, o_bf16=None):
+    eo, el = max_err(o32, o_ref), max_err(lse, l_ref)
+    msg = f"{tag}: max|O-ref| {eo:.3e}  max|LSE-ref| {el:.3e}"
+    if o_bf16 is not None:
+        eb = max_err(o_bf16, o_ref)
+        nb = int((np.abs(f64(o_bf16) - o_ref) > TOL_O).sum())
+        msg += f"  bf16 O {eb:.3e} ({nb} elems > {TOL_O})"
+        assert np.array_equal(f64(o_bf16), rne_bf16(o32)), "bf16 output is not RNE of the fp32 output"
+    log(msg)
+    assert eo <= TOL_O and el <= TOL_LSE, msg
+
+
+def test_ring_small_d64_seeded_order():
+    w = get("ring_small_d64")
+    q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    qd, kd, vd = _to_dev(q, k, v)
+    out, lse, o_acc = ba.ring_forward(qd, kd, vd, w.n_chunks, order)
+    torch.cuda.synchronize()
+    o_ref, l_ref = ring_attention_forward(f64(q), f64(k), f64(v), order, w.chunk_len)
+    _check_pair(f"{w.name} order={order}", o_acc, lse, o_ref, l_ref, out)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S,Hq,Hkv,causal", [(1000, 2, 2, True), (333, 8, 2, True), (777, 4, 4, False),
+                                             (128, 2, 1, True), (1, 2, 2, True)])
+def test_one_shot(D, S, Hq, Hkv, causal):
+    q, k, v = make_inputs(1, S, Hq, Hkv, D, seed=S + D)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = torch.full((1, S, Hq, D), float("nan"), device=dev())
+    ob = torch.empty((1, S, Hq, D), device=dev(), dtype=torch.bfloat16)
+    lse = torch.full((1, Hq, S), float("nan"), device=dev())
+    ba.blockattn_fwd(qd, kd, vd, o, lse, causal=causal, o_final=ob)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), causal=causal)
+    _check_pair(f"one-shot D{D} S{S} Hq{Hq} Hkv{Hkv} causal={causal}", o, lse, o_ref, l_ref, ob)
+
+
+def test_one_shot_bf16_output_and_batch():
+    B, S, H, D = 3, 300, 2, 128
+    q, k, v = make_inputs(B, S, H, H, D, seed=5)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = torch.empty((B, S, H, D), device=dev(), dtype=torch.bfloat16)
+    lse = torch.empty((B, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd, vd, o, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    eo, el = max_err(o, o_ref), max_err(lse, l_ref)
+    log(f"bf16-direct B{B}: O {eo:.3e} LSE {el:.3e}")
+    assert eo <= 1.5e-2 and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("n_chunks,S", [(5, 1024), (3, 1000), (8, 2048)])
+def test_ring_orders_match_one_shot(n_chunks, S):
+    H, D = 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=n_chunks)
+    qd, kd, vd = _to_dev(q, k, v)
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    for seed in range(3):
+        order = chunk_order(n_chunks, seed=seed)
+        out, lse, o_acc = ba.ring_forward(qd, kd, vd, n_chunks, order)
+        torch.cuda.synchronize()
+        _check_pair(f"ring n={n_chunks} S={S} order={order}", o_acc, lse, o_ref, l_ref, out)
+
+
+def test_chunk_with_offsets_and_empty_rows():
+    """One chunk at an arbitrary offset: rows before it get the empty pair (0, -inf)."""
+    Sq, Sk, H, D, q0, k0 = 300, 200, 2, 128, 50, 120
+    q, _, _ = make_inputs(1, Sq, H, H, D, seed=11)
+    _, k, v = make_inputs(1, Sk, H, H, D, seed=12)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = torch.full((1, Sq, H, D), float("nan"), device=dev())
+    lse = torch.full((1, H, Sq), float("nan"), device=dev())
+    ba.blockattn_fwd(qd, kd, vd, o, lse, q_pos0=q0, k_pos0=k0)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), q_pos0=q0, k_pos0=k0)
+    assert np.array_equal(np.isinf(f64(lse)), np.isinf(l_ref))
+    assert np.all(f64(o)[:, :k0 - q0] == 0.0)
+    _check_pair("offset chunk", o, lse, o_ref, l_ref)
+
+
+def test_accumulate_empty_chunk_is_identity():
+    S, H, D = 256, 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=13)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = torch.empty((1, S, H, D), device=dev())
+    lse = torch.empty((1, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd, vd, o, lse)
+    o0, l0 = o.clone(), lse.clone()
+    fin = torch.empty((1, S, H, D), device=dev(), dtype=torch.bfloat16)
+    # a chunk entirely after every query contributes nothing
+    ba.blockattn_fwd(qd, kd, vd, o, lse, mode=ba.BA_ACCUMULATE, k_pos0=S, o_final=fin)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+    assert torch.equal(fin, o0.to(torch.bfloat16))
+
+
+def test_peaked_softmax():
+    S, H, D = 1024, 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=21, q_scale=4.0)
+    qd, kd, vd = _to_dev(q, k, v)
+    order = chunk_order(4, seed=3)
+    out, lse, o_acc = ba.ring_forward(qd, kd, vd, 4, order)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    _check_pair("peaked softmax (Q x4)", o_acc, lse, o_ref, l_ref, out)
+
+
+def test_forward_bitwise_deterministic():
+    S, H, D = 2048, 4, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=31)
+    qd, kd, vd = _to_dev(q, k, v)
+    order = chunk_order(4, seed=0)
+    r1 = [t.clone() for t in ba.ring_forward(qd, kd, vd, 4, order)]
+    r2 = ba.ring_forward(qd, kd, vd, 4, order)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
+def test_lse_merge_standalone(part_dtype):
+    B, S, H, D = 2, 200, 3, 128
+    g = torch.Generator().manual_seed(7)
+    oa = torch.randn(B, S, H, D, generator=g)
+    ob = torch.randn(B, S, H, D, generator=g).to(part_dtype)
+    la = torch.randn(B, H, S, generator=g) * 3
+    lb = torch.randn(B, H, S, generator=g) * 3
+    la[0, 0, :10] = float("-inf")
+    lb[0, 0, 5:15] = float("-inf")
+    oa[0, :10, 0] = float("nan")      # O of an empty pair is never read
+    o_ref, l_ref = lse_merge(f64(oa), f64(la), f64(ob), f64(lb))
+    oad, lad, obd, lbd = _to_dev(oa, la, ob, lb)
+    fin = torch.empty((B, S, H, D), device=dev(), dtype=torch.bfloat16)
+    ba.lse_merge(oad, lad, obd, lbd, o_final=fin)
+    torch.cuda.synchronize()
+    eo, el = max_err(oad, o_ref), max_err(lad, l_ref)
+    log(f"lse_merge part={part_dtype}: O {eo:.3e} LSE {el:.3e}")
+    assert eo <= 1e-4 and el <= 1e-4
+    assert np.array_equal(f64(fin), rne_bf16(oad))
+
+
+def test_fused_merge_equals_standalone_merge():
+    """A ring step in ACCUMULATE mode equals OVERWRITE into a scratch pair + lse_merge."""
+    S, H, D = 1024, 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=41)
+    qd, kd, vd = _to_dev(q, k, v)
+    c0, c1 = 256, 512
+    o1 = torch.empty((1, S, H, D), device=dev()); l1 = torch.empty((1, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd[:, :c0], vd[:, :c0], o1, l1)
+    o2, l2 = o1.clone(), l1.clone()
+    ba.blockattn_fwd(qd, kd[:, c0:c1], vd[:, c0:c1], o1, l1, mode=ba.BA_ACCUMULATE, k_pos0=c0)
+    op = torch.empty((1, S, H, D), device=dev()); lp = torch.empty((1, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd[:, c0:c1], vd[:, c0:c1], op, lp, k_pos0=c0)
+    ba.lse_merge(o2, l2, op, lp)
+    torch.cuda.synchronize()
+    assert max_err(o1, f64(o2)) <= 1e-5 and max_err(l1, f64(l2)) <= 1e-5
+
+
+@pytest.mark.parametrize("Hq,Hkv,shift_head0", [(4, 4, 2), (8, 2, 4), (2, 2, 2)])
+def test_s2_forward(Hq, Hkv, shift_head0):
+    S, G, D = 2048, 512, 128
+    q, k, v = make_inputs(1, S, Hq, Hkv, D, seed=51)
+    qd, kd, vd = _to_dev(q, k, v)
+    o, lse = ba.s2_forward(qd, kd, vd, G, shift_head0, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), s2=S2Spec(G, shift_head0, S))
+    _check_pair(f"s2 fwd Hq{Hq} Hkv{Hkv} shift_head0={shift_head0}", o, lse, o_ref, l_ref)
+
+
+def test_s2_full_group_no_shift_equals_causal():
+    S, G, H, D = 1024, 1024, 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=52)
+    qd, kd, vd = _to_dev(q, k, v)
+    o1, l1 = ba.s2_forward(qd, kd, vd, G, H, o_dtype=torch.float32)
+    o2 = torch.empty_like(o1); l2 = torch.empty_like(l1)
+    ba.blockattn_fwd(qd, kd, vd, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- full sizes, sampled rows
+
+def _sample_rows(S, C, rng, n_random=24):
+    rows = {0, 1, 63, 64, 127, 128, S - 1, S - 2}
+    for c in range(0, S, C):
+        rows.update({c, c + 1, c - 1 if c else 0})
+    rows.update(int(x) for x in rng.integers(0, S, n_random))
+    return sorted(r for r in rows if 0 <= r < S)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_s32k_ring8", "gqa_llama3_8b_s128k_ring16",
+                                  "llama2_13b_s64k_ring8_train"])
+def test_full_size_ring_sampled(name):
+    w = get(name)
+    log(f"full-size ring forward {name}: generating inputs")
+    q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    qd, kd, vd = _to_dev(q, k, v)
+    out, lse, o_acc = ba.ring_forward(qd, kd, vd, w.n_chunks, order)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    heads = sorted({0, w.heads_q - 1, int(rng.integers(1, w.heads_q - 1))})
+    rows = _sample_rows(w.seqlen, w.chunk_len, rng)
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    worst_o = worst_l = 0.0
+    for h in heads:
+        o_ref, l_ref = rows_forward(qn, kn, vn, 0, h, rows)
+        o_got = o_acc[0, rows, h].cpu()
+        worst_o = max(worst_o, max_err(o_got, o_ref))
+        worst_l = max(worst_l, max_err(lse[0, h, rows].cpu(), l_ref))
+        assert np.array_equal(f64(out[0, rows, h]), rne_bf16(o_got))
+    log(f"{name} order={order} heads={heads} rows={len(rows)}: O {worst_o:.3e} LSE {worst_l:.3e}")
+    assert worst_o <= TOL_O and worst_l <= TOL_LSE
+    assert not torch.isnan(o_acc).any()
