@@ -1,0 +1,185 @@
+"""Throughput of the ring-step attention hot path on one MI355X.
+
+A step is one pass of the Llama-2-7B-shaped long-context forward: Q, K, V
+[1, 32768, 32, 128] bf16 (i.i.d. N(0,1), seed 0), the key/value sequence streamed
+as 8 ring-step chunks of 4096 in a seeded random order, every step merging its
+partial (O, LSE) pair into the running pair, the last one also storing the
+final bf16 output.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: attention TFLOP/s (algorithmic flops: 4*D per allowed
+causal (query, key) pair), the dominant kernel's roofline fraction against the
+dense bf16 MFMA peak, and the CPU oracle timed on a bounded sample of the same
+workload.  Other workloads: --workload <name> (see workloads/configs.py).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal attention fwd/bwd TFLOP/s and % bf16 MFMA peak at S=32K-128K, D=128"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+FWD_SRC = os.path.join(ROOT, "long_context_exact_blockattn_amd", "csrc", "ba_fwd.h")
+
+
+def _src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_path):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_key}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != _src_sha(src_path):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_ring_forward(w, steps, warmup):
+    import torch
+
+    import long_context_exact_blockattn_amd as ba
+    from long_context_exact_blockattn_amd import _lib
+    from workloads import chunk_bounds, chunk_order, make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    bounds = chunk_bounds(w.seqlen, w.n_chunks)
+    b, s, hq, d = q.shape
+    o_acc = torch.empty(b, s, hq, d, device=dev, dtype=torch.float32)
+    lse = torch.empty(b, hq, s, device=dev, dtype=torch.float32)
+    out = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
+    n = len(order)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+
+    def step(events=None):
+        for t, c in enumerate(order):
+            c0, c1 = bounds[c]
+            if events is not None:
+                events[t].record()
+            _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
+                               mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
+                               o_final=out if t == n - 1 else None, k_pos0=c0)
+        if events is not None:
+            events[n].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [ev[i][t].elapsed_time(ev[i][t + 1]) for i in range(steps) for t in range(n)]
+    assert not torch.isnan(out).any(), "NaN in output"
+    return {"wall_s": wall, "launch_ms": launch_ms, "launches_per_step": n, "order": order,
+            "kernel": "fwd_kernel<128>", "src": FWD_SRC}
+
+
+def cpu_baseline(w, budget_heads=1):
+    """The oracle as it stands, on one query head of the same workload (all ring steps)."""
+    import numpy as np
+
+    from oracle import ring_attention_forward
+    from workloads import chunk_order, make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
+    heads = list(range(budget_heads))
+    kv_heads = sorted({h // (w.heads_q // w.heads_kv) for h in heads})
+    qn = q[:, :, heads].float().numpy().astype(np.float64)
+    kn = k[:, :, kv_heads].float().numpy().astype(np.float64)
+    vn = v[:, :, kv_heads].float().numpy().astype(np.float64)
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    t0 = time.perf_counter()
+    ring_attention_forward(qn, kn, vn, order, w.chunk_len)
+    dt = time.perf_counter() - t0
+    flop = w.fwd_flop() * len(heads) / w.heads_q
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: query head 0 of {w.heads_q} at full S={w.seqlen}, all {w.n_chunks} ring "
+                      f"steps in the seeded order, numpy float64; {dt:.1f} s for {flop:.3e} algorithmic flop"}
+
+
+def copy_calibration(reps):
+    """A plain copy kernel of known size: reads and writes exactly 1 GiB per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(reps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": max(reps, 1)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama2_7b_s32k_ring8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the multi-GPU ring (key/value exchange between "
+              "devices) is not part of this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import get
+    w = get(args.workload)
+    if w.s2_group is not None or w.backward:
+        print(f"workload {w.name} is not a forward ring workload; use a forward ring workload", file=sys.stderr)
+        sys.exit(2)
+    r = run_ring_forward(w, args.steps, args.warmup)
+    ms_per_step = r["wall_s"] * 1e3 / args.steps
+    flop = w.fwd_flop()
+    tflops = flop / (ms_per_step * 1e-3) / 1e12
+    launch_ms = r["launch_ms"]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    achieved = flop / r["launches_per_step"] / (avg_launch_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic("fwd_kernel_d128", r["src"]),
+                "kernel": r["kernel"], "avg_launch_ms": round(avg_launch_ms, 4),
+                "launches_per_step": r["launches_per_step"]}
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks,
+                   "chunk_order": r["order"], "causal": True, "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
