@@ -1,15 +1,432 @@
-// Backward kernels (placeholder until the gfx950 backward lands).
+// Backward kernels: gradient of <dO, O> for one ring step (one key/value chunk).
+//
+// With S = tau Q K^T, P = exp(S - LSE) (LSE of the FINAL output, all chunks),
+// dP = dO V^T and dS = P (dP - delta), delta_i = sum_d dO_id O_id:
+//   dV = P^T dO,  dK = tau dS^T Q,  dQ = tau dS K.
+// The pages train with exact attention (project page "How It Works"; LongLoRA
+// and Ring Attention summaries) without printing the gradient; this is the
+// analytic one.  Three kernels, no atomics:
+//   delta_kernel  rowsum(dO * O) -> delta                            (HBM-bound)
+//   dkdv_kernel   key/value-stationary: each lane owns one key; S, dP, and the
+//                 dV, dK contractions over the query tiles the mask allows;
+//                 GQA sums the group's query heads inside the item
+//   dq_kernel     query-stationary: each lane owns one query row; S, dP and
+//                 dQ over the key tiles the mask allows, then dq_acc += tau dQ
+// Every MFMA is v_mfma_f32_32x32x16_bf16 with operands arranged as in the
+// forward kernel (see ba_fwd.h): the stationary side is the B operand held in
+// registers, tiles of the streamed side are read from LDS, directly for
+// contractions over D and through ds_read_b64_tr_b16 for contractions over
+// the streamed rows.
 #pragma once
 
-#include "../../include/blockattn.h"
 #include "ba_common.h"
+#include "ba_schedule.h"
 
 namespace ba {
 
-static inline int bwd_impl(const ba_desc*, const ba_s2_desc*, const void*, const void*, const void*,
-                           const void*, const void*, const float*, float*, float*, void*, void*,
-                           int32_t, void*, int32_t, hipStream_t) {
-  return BA_ERR_UNSUPPORTED;
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;
+  float* delta;
+  float* dq_acc;
+  void* dk;
+  void* dv;
+  bf16* dq_final;
+  int64_t qs_b, qs_s, qs_h;
+  int64_t ks_b, ks_s, ks_h;
+  int64_t Sq, Sk, q_pos0, k_pos0;
+  int32_t B, Hq, Hkv, grp;
+  int32_t causal, s2_group, s2_shift_head0;
+  int32_t dkv_f32, finalize;
+  float scale, scale_log2;
+  int64_t n_tiles;  // query tiles (dq_kernel) or key tiles (dkdv_kernel) per head
+  int64_t n_items;
+};
+
+constexpr int kDqBM = 128;   // query rows per dq item (4 waves x 32)
+constexpr int kDqBN = 64;    // key rows per streamed tile
+constexpr int kKvBN = 128;   // keys per dkdv item (4 waves x 32)
+constexpr int kKvBM = 64;    // query rows per streamed tile
+constexpr int kBwdThreads = 256;
+
+__device__ __forceinline__ Sched bwd_sched(const BwdArgs& a, int head, int BM, int BN) {
+  Sched sc;
+  sc.Sq = a.Sq; sc.Sk = a.Sk; sc.q_pos0 = a.q_pos0; sc.k_pos0 = a.k_pos0;
+  sc.causal = a.causal; sc.s2_group = a.s2_group;
+  sc.s2_shift = (a.s2_group > 0 && head >= a.s2_shift_head0) ? a.s2_group / 2 : 0;
+  sc.BM = BM; sc.BN = BN;
+  return sc;
+}
+
+// ---------------------------------------------------------------- delta = rowsum(dO * O)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t n_threads) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int CPR = D / 8;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rowid = g / CPR;
+  const int c = (int)(g % CPR);
+  float acc = 0.f;
+  int64_t b = 0, s = 0;
+  int h = 0;
+  if (g < n_threads) {
+    h = (int)(rowid % a.Hq);
+    s = (rowid / a.Hq) % a.Sq;
+    b = rowid / ((int64_t)a.Hq * a.Sq);
+    const int64_t off = b * a.qs_b + s * a.qs_s + (int64_t)h * a.qs_h + 8 * c;
+    const bf16x8 x = *(const bf16x8*)(a.dout + off);
+    const bf16x8 y = *(const bf16x8*)(a.o + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+  }
+  // CPR consecutive lanes of one wavefront hold one row
+#pragma unroll
+  for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (g < n_threads && c == 0) a.delta[(b * a.Hq + h) * a.Sq + s] = acc;
+#endif
+}
+
+// ---------------------------------------------------------------- dQ (query-stationary)
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = kDqBM, BN = kDqBN;
+  constexpr int ROW = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int RPP = kBwdThreads / CPR;
+  constexpr int NPASS = BN / RPP;
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+
+  const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
+  const int64_t bh = pid / a.n_tiles;
+  const int64_t w = pid % a.n_tiles;
+  const int b = (int)(bh / a.Hq);
+  const int h = (int)(bh % a.Hq);
+  const int kvh = h / a.grp;
+  const Sched sc = bwd_sched(a, h, BM, BN);
+  const QTile qt = make_qtile(sc, qtile_of_rank(sc, a.n_tiles, w));
+  const bool empty = qt.kt_end <= qt.kt_begin;
+  if (empty && !a.finalize) return;
+
+  const int rloc = wave * 32 + l32;
+  const bool row_ok = rloc < qt.rows;
+  const int64_t row = qt.row0 + rloc;
+  const int64_t qcpos = qt.cpos0 + rloc;
+  const int64_t wave_cmin = qt.cpos0 + wave * 32;
+  const int64_t wave_cmax = wave_cmin + 31;
+  const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
+  const int64_t qoff = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h;
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
+
+  if (!empty) {
+    const float lse2 = row_ok ? a.lse[lse_idx] * kLog2e : INFINITY;
+    const float dlt = row_ok ? a.delta[lse_idx] : 0.f;
+    bf16x8 qf[KK], df[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = row_ok ? *(const bf16x8*)(a.q + qoff + 16 * kk + 8 * hl) : bf16x8{};
+      df[kk] = row_ok ? *(const bf16x8*)(a.dout + qoff + 16 * kk + 8 * hl) : bf16x8{};
+    }
+    const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+    const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+    u32x4 st[NPASS];
+    auto gload = [&](const bf16* base, int64_t kt) {
+      const KTile t = make_ktile(sc, kt);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = p * RPP + tid / CPR;
+        const int c = tid % CPR;
+        st[p] = r < t.rows ? *(const u32x4*)(base + (t.row0 + r) * a.ks_s + 8 * c) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto lstore = [&](bf16* dst) {
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const int r = p * RPP + tid / CPR;
+        const int c = tid % CPR;
+        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[p];
+      }
+    };
+    gload(kbase, qt.kt_begin);
+    lstore(smem[0][0]);
+    gload(vbase, qt.kt_begin);
+    lstore(smem[0][1]);
+    __syncthreads();
+
+    const int gi = lane & 15;
+    const int dsub = 16 * ((lane >> 4) & 1);
+    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; ++kt) {
+      const int buf = (int)((kt - qt.kt_begin) & 1);
+      const bool has_next = kt + 1 < qt.kt_end;
+      if (has_next) gload(kbase, kt + 1);
+      const KTile t = make_ktile(sc, kt);
+      const bf16* Ks = smem[buf][0];
+      const bf16* Vs = smem[buf][1];
+      const bool active = !(a.causal && t.cpos0 > wave_cmax);
+      const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && has_next) {
+          lstore(smem[buf ^ 1][0]);
+          gload(vbase, kt + 1);
+        }
+        if (!active) continue;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 kf = *(const bf16x8*)(&Ks[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
+          s = mfma32(kf, qf[kk], s);
+          const bf16x8 vf = *(const bf16x8*)(&Vs[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
+          dp = mfma32(vf, df[kk], dp);
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -lse2));
+          if (need_mask) {
+            const bool ok = key < t.rows && (!a.causal || t.cpos0 + key <= qcpos);
+            p = ok ? p : 0.f;
+          }
+          dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dlt));
+        }
+        // dQ^T += K^T dS^T: K^T operand read transposed from the [key][d] tile
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const int k0 = kb * 32 + 16 * c2 + 4 * hl + (gi >> 2);
+            const int dcol = 32 * db + dsub + 4 * (gi & 3);
+            const bf16x4 x0 = lds_read_tr16(&Ks[k0 * ROW + dcol]);
+            const bf16x4 x1 = lds_read_tr16(&Ks[(k0 + 8) * ROW + dcol]);
+            const bf16x8 kt_op = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            dqacc[db] = mfma32(kt_op, dsf[c2], dqacc[db]);
+          }
+        }
+      }
+      if (has_next) lstore(smem[buf ^ 1][1]);
+      __syncthreads();
+    }
+  }
+
+  if (!row_ok) return;
+  const int64_t obase = qoff + 4 * hl;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t off = obase + 32 * db + 8 * g;
+      f32x4 val = *(const f32x4*)(a.dq_acc + off);
+      if (!empty) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(a.scale, dqacc[db][4 * g + e], val[e]);
+        *(f32x4*)(a.dq_acc + off) = val;
+      }
+      if (a.finalize) {
+        bf16x4 bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
+        *(bf16x4*)(a.dq_final + off) = bv;
+      }
+    }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------- dK, dV (key/value-stationary)
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = kKvBM, BN = kKvBN;
+  constexpr int ROW = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int RPP = kBwdThreads / CPR;
+  constexpr int NPASS = BM / RPP;
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 qs[2][BM * ROW];
+  __shared__ __attribute__((aligned(16))) bf16 dos[2][BM * ROW];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
+  __shared__ __attribute__((aligned(16))) float del_s[2][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+
+  const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
+  const int64_t bkv = pid / a.n_tiles;
+  const int64_t w = pid % a.n_tiles;
+  const int b = (int)(bkv / a.Hkv);
+  const int kvh = (int)(bkv % a.Hkv);
+  const int h0 = kvh * a.grp;
+  const Sched sc = bwd_sched(a, h0, BM, BN);  // every head of the group shares the shift
+  const KVItem it = make_kv_item(sc, ktile_of_rank(sc, a.n_tiles, w));
+
+  const int kloc = wave * 32 + l32;
+  const bool key_ok = kloc < it.krows;
+  const int64_t krow = it.krow0 + kloc;
+  const int64_t kcpos = it.kcpos0 + kloc;
+  const int64_t wave_kmin = it.kcpos0 + wave * 32;
+  const int64_t wave_kmax = wave_kmin + 31;
+  const int64_t koff = (int64_t)b * a.ks_b + krow * a.ks_s + (int64_t)kvh * a.ks_h;
+
+  bf16x8 kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kf[kk] = key_ok ? *(const bf16x8*)(a.k + koff + 16 * kk + 8 * hl) : bf16x8{};
+    vf[kk] = key_ok ? *(const bf16x8*)(a.v + koff + 16 * kk + 8 * hl) : bf16x8{};
+  }
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+
+  const int64_t nqt = it.qt_end > it.qt_begin ? it.qt_end - it.qt_begin : 0;
+  const int64_t n_iter = nqt * a.grp;
+  if (n_iter > 0) {
+    u32x4 st[NPASS];
+    auto tile_of = [&](int64_t i, int* head, QTile* t) {
+      *head = h0 + (int)(i / nqt);
+      *t = make_qtile(sc, it.qt_begin + i % nqt);
+    };
+    auto gload = [&](const bf16* base, int64_t i) {
+      int hh; QTile t; tile_of(i, &hh, &t);
+      const bf16* p = base + (int64_t)b * a.qs_b + (int64_t)hh * a.qs_h;
+#pragma unroll
+      for (int pp = 0; pp < NPASS; ++pp) {
+        const int r = pp * RPP + tid / CPR;
+        const int c = tid % CPR;
+        st[pp] = r < t.rows ? *(const u32x4*)(p + (t.row0 + r) * a.qs_s + 8 * c) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto lstore = [&](bf16* dst) {
+#pragma unroll
+      for (int pp = 0; pp < NPASS; ++pp) {
+        const int r = pp * RPP + tid / CPR;
+        const int c = tid % CPR;
+        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[pp];
+      }
+    };
+    auto stats = [&](int64_t i, int buf) {
+      if (tid < BM) {
+        int hh; QTile t; tile_of(i, &hh, &t);
+        const bool ok = tid < t.rows;
+        const int64_t li = ((int64_t)b * a.Hq + hh) * a.Sq + t.row0 + tid;
+        lse_s[buf][tid] = ok ? a.lse[li] * kLog2e : INFINITY;
+        del_s[buf][tid] = ok ? a.delta[li] : 0.f;
+      }
+    };
+    gload(a.q, 0);
+    lstore(qs[0]);
+    gload(a.dout, 0);
+    lstore(dos[0]);
+    stats(0, 0);
+    __syncthreads();
+
+    const int gi = lane & 15;
+    const int dsub = 16 * ((lane >> 4) & 1);
+    for (int64_t i = 0; i < n_iter; ++i) {
+      const int buf = (int)(i & 1);
+      const bool has_next = i + 1 < n_iter;
+      if (has_next) gload(a.q, i + 1);
+      int hh; QTile t; tile_of(i, &hh, &t);
+      const bf16* Qs = qs[buf];
+      const bf16* Ds = dos[buf];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (qb == 1 && has_next) {
+          lstore(qs[buf ^ 1]);
+          gload(a.dout, i + 1);
+        }
+        const int64_t qc0 = t.cpos0 + qb * 32;
+        if (a.causal && wave_kmin > qc0 + 31) continue;  // every pair of the block is masked
+        const bool need_mask = (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > qc0);
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 qa = *(const bf16x8*)(&Qs[(qb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
+          s = mfma32(qa, kf[kk], s);
+          const bf16x8 da = *(const bf16x8*)(&Ds[(qb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
+          dp = mfma32(da, vf[kk], dp);
+        }
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q4 = qb * 32 + 8 * g + 4 * hl;
+          const f32x4 l4 = *(const f32x4*)(&lse_s[buf][q4]);
+          const f32x4 d4 = *(const f32x4*)(&del_s[buf][q4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -l4[e]));
+            if (need_mask) {
+              const bool ok = key_ok && (!a.causal || kcpos <= qc0 + 8 * g + 4 * hl + e);
+              p = ok ? p : 0.f;
+            }
+            pf[r >> 3][r & 7] = (bf16)p;
+            dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - d4[e]));
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const int q0 = qb * 32 + 16 * c2 + 4 * hl + (gi >> 2);
+            const int dcol = 32 * db + dsub + 4 * (gi & 3);
+            const bf16x4 y0 = lds_read_tr16(&Ds[q0 * ROW + dcol]);
+            const bf16x4 y1 = lds_read_tr16(&Ds[(q0 + 8) * ROW + dcol]);
+            dvacc[db] = mfma32(__builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7), pf[c2], dvacc[db]);
+            const bf16x4 x0 = lds_read_tr16(&Qs[q0 * ROW + dcol]);
+            const bf16x4 x1 = lds_read_tr16(&Qs[(q0 + 8) * ROW + dcol]);
+            dkacc[db] = mfma32(__builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), dsf[c2], dkacc[db]);
+          }
+        }
+      }
+      if (has_next) {
+        lstore(dos[buf ^ 1]);
+        stats(i + 1, buf ^ 1);
+      }
+      __syncthreads();
+    }
+  }
+
+  if (!key_ok) return;
+  const int64_t obase = koff + 4 * hl;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t off = obase + 32 * db + 8 * g;
+      f32x4 kv4, vv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv4[e] = a.scale * dkacc[db][4 * g + e];
+        vv4[e] = dvacc[db][4 * g + e];
+      }
+      if (a.dkv_f32) {
+        *(f32x4*)((float*)a.dk + off) = kv4;
+        *(f32x4*)((float*)a.dv + off) = vv4;
+      } else {
+        bf16x4 kb4, vb4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { kb4[e] = (bf16)kv4[e]; vb4[e] = (bf16)vv4[e]; }
+        *(bf16x4*)((bf16*)a.dk + off) = kb4;
+        *(bf16x4*)((bf16*)a.dv + off) = vb4;
+      }
+    }
+  }
+#endif
 }
 
 }  // namespace ba

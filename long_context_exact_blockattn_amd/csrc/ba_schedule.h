@@ -100,6 +100,58 @@ BA_HD int64_t qtile_of_rank(const Sched& s, int64_t nq, int64_t w) {
   return nq - 1 - w;
 }
 
+// Key/value-stationary items (backward dK/dV): one item owns BN keys starting
+// at key tile kt; the query tiles (of BM rows) it must visit are those holding
+// at least one query the mask allows for some key of the item.
+struct KVItem {
+  int64_t krow0, krows, kcpos0;  // as KTile
+  int64_t qt_begin, qt_end;      // query tiles to visit
+};
+
+BA_HD KVItem make_kv_item(const Sched& s, int64_t kt) {
+  KVItem it;
+  const int64_t nq = num_qtiles(s);
+  if (s.s2_group > 0) {
+    const int64_t r0 = kt * s.BN;
+    it.krow0 = (r0 + s.s2_shift) % s.Sk;
+    it.krows = s.BN;
+    it.kcpos0 = r0;
+    const int64_t gend = (r0 / s.s2_group + 1) * s.s2_group;  // end of the key's group (rolled)
+    it.qt_begin = r0 / s.BM;
+    it.qt_end = gend / s.BM;
+    return it;
+  }
+  it.krow0 = kt * s.BN;
+  it.krows = s.Sk - it.krow0 < s.BN ? s.Sk - it.krow0 : s.BN;
+  it.kcpos0 = s.k_pos0 + it.krow0;
+  it.qt_end = nq;
+  if (!s.causal) {
+    it.qt_begin = 0;
+  } else {
+    // first query row i with q_pos0 + i >= kcpos0
+    const int64_t first = it.kcpos0 - s.q_pos0;
+    it.qt_begin = first <= 0 ? 0 : (first >= s.Sq ? nq : first / s.BM);
+  }
+  return it;
+}
+
+BA_HD int64_t num_ktiles(const Sched& s) { return ceil_div(s.Sk, s.BN); }
+
+// Visiting order of key tiles inside one (batch, key/value head): most query
+// tiles first.
+BA_HD int64_t ktile_of_rank(const Sched& s, int64_t nk, int64_t w) {
+  if (s.s2_group > 0) {
+    const int64_t per_group = s.s2_group / s.BN;
+    const int64_t ngroups = nk / per_group;
+    const int64_t pos = w / ngroups;      // position inside the group, ascending
+    const int64_t g = w % ngroups;
+    return g * per_group + pos;
+  }
+  // causal: a later key tile never sees more query tiles than an earlier one,
+  // so ascending order is longest first (and any order is, without a mask)
+  return w;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  The
 // remap gives XCD x the contiguous logical range [x*per, (x+1)*per), so the
 // query tiles of one head (which read the same keys and values) share one L2.

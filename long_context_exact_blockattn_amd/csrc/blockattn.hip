@@ -103,6 +103,77 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   return launched();
 }
 
+int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* k, const void* v,
+             const void* o, const void* dout, const float* lse, float* delta, float* dq_acc, void* dk,
+             void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags, hipStream_t stream) {
+  int r = check_desc(d);
+  if (r) return r;
+  if (s2 && (r = check_s2(d, s2))) return r;
+  if (flags & ~(BA_BWD_COMPUTE_DELTA | BA_BWD_FINALIZE_DQ)) return BA_ERR_MODE;
+  if (dkv_dtype != BA_F32 && dkv_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;
+  if (d->batch == 0 || (d->seqlen_q == 0 && d->seqlen_k == 0)) return BA_OK;
+  const bool finalize = (flags & BA_BWD_FINALIZE_DQ) != 0;
+  if (d->seqlen_q > 0 && (!q || !o || !dout || !lse || !delta || !dq_acc)) return BA_ERR_NULL;
+  if (d->seqlen_q > 0 && finalize && !dq_final) return BA_ERR_NULL;
+  if (d->seqlen_k > 0 && (!k || !v || !dk || !dv)) return BA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq_acc, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dq_final, 16) ||
+      !aligned(lse, 4) || !aligned(delta, 4))
+    return BA_ERR_ALIGN;
+
+  BwdArgs a;
+  a.q = (const bf16*)q; a.k = (const bf16*)k; a.v = (const bf16*)v;
+  a.o = (const bf16*)o; a.dout = (const bf16*)dout;
+  a.lse = lse; a.delta = delta; a.dq_acc = dq_acc; a.dk = dk; a.dv = dv;
+  a.dq_final = (bf16*)dq_final;
+  a.qs_b = d->q_stride[0]; a.qs_s = d->q_stride[1]; a.qs_h = d->q_stride[2];
+  a.ks_b = d->kv_stride[0]; a.ks_s = d->kv_stride[1]; a.ks_h = d->kv_stride[2];
+  a.Sq = d->seqlen_q; a.Sk = d->seqlen_k; a.q_pos0 = d->q_pos0; a.k_pos0 = d->k_pos0;
+  a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.grp = d->heads_q / d->heads_kv;
+  a.causal = s2 ? 1 : d->causal;
+  a.s2_group = s2 ? s2->group : 0;
+  a.s2_shift_head0 = s2 ? s2->shift_head0 : 0;
+  a.dkv_f32 = dkv_dtype == BA_F32;
+  a.finalize = finalize;
+  a.scale = scale_of(d);
+  a.scale_log2 = a.scale * kLog2e;
+  const bool d128 = d->head_dim == 128;
+
+  if ((flags & BA_BWD_COMPUTE_DELTA) && d->seqlen_q > 0) {
+    const int64_t n = (int64_t)d->batch * d->seqlen_q * d->heads_q * (d->head_dim / 8);
+    const int64_t blocks = ceil_div(n, 256);
+    if (blocks > 0x7fffffffLL) return BA_ERR_SHAPE;
+    if (d128)
+      hipLaunchKernelGGL(bwd_delta_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+    else
+      hipLaunchKernelGGL(bwd_delta_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+    if ((r = launched())) return r;
+  }
+  if (d->seqlen_k > 0) {
+    BwdArgs b = a;
+    b.n_tiles = ceil_div(d->seqlen_k, kKvBN);
+    b.n_items = (int64_t)d->batch * d->heads_kv * b.n_tiles;
+    if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
+    if (d128)
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+    if ((r = launched())) return r;
+  }
+  if (d->seqlen_q > 0) {
+    BwdArgs b = a;
+    b.n_tiles = ceil_div(d->seqlen_q, kDqBM);
+    b.n_items = (int64_t)d->batch * d->heads_q * b.n_tiles;
+    if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
+    if (d128)
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+    if ((r = launched())) return r;
+  }
+  return BA_OK;
+}
+
 }  // namespace
 
 extern "C" {

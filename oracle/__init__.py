@@ -14,6 +14,9 @@ from .attention import (
     S2Spec,
     allowed_mask,
     attention_backward,
+    backward_delta,
+    cols_backward_dkdv,
+    rows_backward_dq,
     attention_forward,
     default_scale,
     lse_merge,
@@ -26,6 +29,9 @@ __all__ = [
     "S2Spec",
     "allowed_mask",
     "attention_backward",
+    "backward_delta",
+    "cols_backward_dkdv",
+    "rows_backward_dq",
     "attention_forward",
     "default_scale",
     "lse_merge",

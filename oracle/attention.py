@@ -256,3 +256,66 @@ def attention_backward(q, k, v, do, *, scale=None, causal: bool = True,
                 dk[b, :, kvh, :] += tau * (ds.T @ Q)
                 dv[b, :, kvh, :] += p.T @ dO
     return dq, dk, dv, o, lse
+
+
+def backward_delta(o, do):
+    """Delta_i = sum_d dO_id O_id, [B, H, S] from [B, S, H, D] inputs (first step of the backward)."""
+    o = np.asarray(o, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    return np.transpose(np.sum(o * do, axis=-1), (0, 2, 1))
+
+
+def rows_backward_dq(q, k, v, do, b: int, h: int, rows: Sequence[int], *, scale=None,
+                     causal: bool = True, s2: Optional[S2Spec] = None):
+    """dQ of selected query rows of one (batch, head), from the definitions above.
+
+    Each row needs only its own full row of probabilities (its LSE), its own
+    output O_i (for Delta_i) and every key/value row.
+    """
+    _, _, hq, d = q.shape
+    hkv = k.shape[2]
+    tau = default_scale(d) if scale is None else float(scale)
+    kvh = _kv_head(h, hq, hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    Q = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    dO = np.asarray(do[b, rows, h, :], dtype=np.float64)
+    K = np.asarray(k[b, :, kvh, :], dtype=np.float64)
+    V = np.asarray(v[b, :, kvh, :], dtype=np.float64)
+    s = tau * (Q @ K.T)
+    p, _ = _softmax_rows(s, allowed_mask(rows, np.arange(K.shape[0]), causal=causal, s2=s2, head=h))
+    O = p @ V
+    delta = np.sum(dO * O, axis=1)
+    ds = p * (dO @ V.T - delta[:, None])
+    return tau * (ds @ K)
+
+
+def cols_backward_dkdv(q, k, v, do, b: int, kvh: int, keys: Sequence[int], *, scale=None,
+                       causal: bool = True, s2: Optional[S2Spec] = None, row_block: int = 1024):
+    """dK and dV of selected key rows of one (batch, key/value head).
+
+    Needs every query row's LSE and output (all keys), so it runs the plain
+    forward over all rows of the query heads that read this key/value head,
+    then sums the selected key columns of dS and P over those rows.
+    """
+    _, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    tau = default_scale(d) if scale is None else float(scale)
+    grp = hq // hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    K = np.asarray(k[b, :, kvh, :], dtype=np.float64)
+    V = np.asarray(v[b, :, kvh, :], dtype=np.float64)
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), d))
+    for h in range(kvh * grp, (kvh + 1) * grp):
+        for r0 in range(0, sq, row_block):
+            r1 = min(sq, r0 + row_block)
+            Q = np.asarray(q[b, r0:r1, h, :], dtype=np.float64)
+            dO = np.asarray(do[b, r0:r1, h, :], dtype=np.float64)
+            s = tau * (Q @ K.T)
+            p, _ = _softmax_rows(s, allowed_mask(np.arange(r0, r1), np.arange(sk), causal=causal, s2=s2, head=h))
+            delta = np.sum(dO * (p @ V), axis=1)
+            pc = p[:, keys]
+            dsc = pc * (dO @ V[keys].T - delta[:, None])
+            dk += tau * (dsc.T @ Q)
+            dv += pc.T @ dO
+    return dk, dv

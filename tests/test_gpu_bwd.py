@@ -1,0 +1,157 @@
+"""GPU parity of the backward (delta, dK/dV, dQ) and of S2 backward against the oracle.
+
+Gate: relative L2 error <= 2e-2 per gradient tensor (dQ, dK, dV) on unit-normal
+bf16 inputs.  The GPU backward consumes the GPU forward's own bf16 O and fp32
+LSE; the oracle recomputes everything from Q, K, V, dO in float64.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_exact_blockattn_amd as ba
+from long_context_exact_blockattn_amd import _lib
+from oracle import S2Spec, attention_backward, backward_delta, cols_backward_dkdv, rows_backward_dq
+from tests.gpu_helpers import TOL_GRAD, dev, f64, log, rel_l2
+from workloads import chunk_order, get, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(*ts):
+    return [t.to(dev()) for t in ts]
+
+
+def _gpu_forward_backward(q, k, v, do, n_chunks=1, order=None, causal=True, dkv_dtype=torch.bfloat16):
+    qd, kd, vd, dod = _to_dev(q, k, v, do)
+    out, lse, _ = ba.ring_forward(qd, kd, vd, n_chunks, order, causal=causal)
+    dq, dk, dv = ba.ring_backward(qd, kd, vd, out, dod, lse, n_chunks, order, causal=causal,
+                                  dkv_dtype=dkv_dtype)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check_grads(tag, got, ref):
+    errs = [rel_l2(g, r) for g, r in zip(got, ref)]
+    log(f"{tag}: rel L2 dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}")
+    assert max(errs) <= TOL_GRAD, errs
+    for g in got:
+        assert not torch.isnan(g).any()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("S,Hq,Hkv,causal", [(1000, 2, 2, True), (333, 8, 2, True), (300, 2, 2, False),
+                                             (64, 4, 1, True)])
+def test_backward_one_shot(D, S, Hq, Hkv, causal):
+    q, k, v, do = make_inputs(1, S, Hq, Hkv, D, seed=S + 7 * D, with_dout=True)
+    got = _gpu_forward_backward(q, k, v, do, causal=causal)
+    dq, dk, dv, _, _ = attention_backward(f64(q), f64(k), f64(v), f64(do), causal=causal)
+    _check_grads(f"bwd one-shot D{D} S{S} Hq{Hq} Hkv{Hkv} causal={causal}", got, (dq, dk, dv))
+
+
+@pytest.mark.parametrize("n_chunks,S", [(4, 1024), (3, 1000), (8, 2048)])
+def test_backward_ring_chunks(n_chunks, S):
+    H, D = 2, 128
+    q, k, v, do = make_inputs(1, S, H, H, D, seed=90 + n_chunks, with_dout=True)
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do))[:3]
+    for seed in range(2):
+        order = chunk_order(n_chunks, seed=seed)
+        got = _gpu_forward_backward(q, k, v, do, n_chunks, order)
+        _check_grads(f"bwd ring n={n_chunks} S={S} order={order}", got, ref)
+
+
+def test_backward_fp32_dkdv_and_batch():
+    B, S, H, D = 2, 400, 2, 128
+    q, k, v, do = make_inputs(B, S, H, H, D, seed=95, with_dout=True)
+    got = _gpu_forward_backward(q, k, v, do, dkv_dtype=torch.float32)
+    assert got[1].dtype == torch.float32
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do))[:3]
+    _check_grads(f"bwd B{B} fp32 dK/dV", got, ref)
+
+
+def test_delta_kernel():
+    """Delta = rowsum(dO * O) on seeded inputs (a call with no key chunk runs only the delta step)."""
+    B, S, H, D = 2, 300, 3, 128
+    g = torch.Generator().manual_seed(3)
+    o = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    od, dod = _to_dev(o, do)
+    q = torch.zeros_like(od)
+    k = torch.zeros((B, 0, H, D), device=dev(), dtype=torch.bfloat16)
+    lse = torch.zeros((B, H, S), device=dev())
+    delta = torch.full((B, H, S), float("nan"), device=dev())
+    dq_acc = torch.zeros((B, S, H, D), device=dev())
+    _lib.blockattn_bwd(q, k, k, od, dod, lse, delta, dq_acc, k, k, flags=_lib.BA_BWD_COMPUTE_DELTA)
+    torch.cuda.synchronize()
+    ref = backward_delta(f64(o), f64(do))
+    err = float(np.abs(f64(delta) - ref).max())
+    log(f"delta max abs err {err:.3e}")
+    assert err <= 1e-4
+
+
+@pytest.mark.parametrize("Hq,Hkv,shift_head0", [(4, 4, 2), (8, 2, 4)])
+def test_s2_backward(Hq, Hkv, shift_head0):
+    S, G, D = 2048, 512, 128
+    q, k, v, do = make_inputs(1, S, Hq, Hkv, D, seed=97, with_dout=True)
+    qd, kd, vd, dod = _to_dev(q, k, v, do)
+    o, lse = ba.s2_forward(qd, kd, vd, G, shift_head0)
+    got = ba.s2_backward(qd, kd, vd, o, dod, lse, G, shift_head0)
+    torch.cuda.synchronize()
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), s2=S2Spec(G, shift_head0, S))[:3]
+    _check_grads(f"s2 bwd Hq{Hq} Hkv{Hkv} shift_head0={shift_head0}", got, ref)
+
+
+def test_s2_backward_llama2_7b_s8k_heads_subset():
+    """S2 workload shape (S=8192, G=2048, 32 heads, heads 16-31 shifted) on 4 of its heads.
+
+    Heads are independent in MHA, so heads {0, 15, 16, 31} (two unshifted, two
+    shifted) are a faithful subset; shift_head0 becomes 2 inside the subset.
+    """
+    w = get("s2attn_llama2_7b_s8k_g2048")
+    q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
+    heads = [0, 15, 16, 31]
+    sub = [t[:, :, heads].contiguous() for t in (q, k, v, do)]
+    qd, kd, vd, dod = _to_dev(*sub)
+    o, lse = ba.s2_forward(qd, kd, vd, w.s2_group, 2)
+    got = ba.s2_backward(qd, kd, vd, o, dod, lse, w.s2_group, 2)
+    torch.cuda.synchronize()
+    ref = attention_backward(*(f64(t) for t in sub), s2=S2Spec(w.s2_group, 2, w.seqlen))[:3]
+    _check_grads("s2 bwd S=8192 G=2048 heads {0,15,16,31}", got, ref)
+
+
+def test_backward_full_size_sampled():
+    """Training-step shape (S=65536, H=40, 8 ring chunks): sampled dQ rows, sampled dK/dV keys.
+
+    Plus properties that hold at any size for every head: sum_j dK_j = 0 and
+    <dV, V> = <dO, O>.
+    """
+    w = get("llama2_13b_s64k_ring8_train")
+    log("full-size backward: generating inputs")
+    q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    qd, kd, vd, dod = _to_dev(q, k, v, do)
+    out, lse, _ = ba.ring_forward(qd, kd, vd, w.n_chunks, order)
+    dq, dk, dv = ba.ring_backward(qd, kd, vd, out, dod, lse, w.n_chunks, order, dkv_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
+    rows = sorted({0, 1, w.seqlen - 1, 4096, 8191, 8192, *map(int, rng.integers(0, w.seqlen, 12))})
+    worst = 0.0
+    for h in (0, w.heads_q - 1):
+        ref = rows_backward_dq(qn, kn, vn, don, 0, h, rows)
+        worst = max(worst, rel_l2(dq[0, rows, h].cpu(), ref))
+    log(f"full-size dQ sampled rows: rel L2 {worst:.3e}")
+    assert worst <= TOL_GRAD
+    keys = sorted({0, 1, w.seqlen - 1, 8191, 8192, *map(int, rng.integers(0, w.seqlen, 6))})
+    dk_ref, dv_ref = cols_backward_dkdv(qn, kn, vn, don, 0, 3, keys, row_block=2048)
+    ek, ev = rel_l2(dk[0, keys, 3].cpu(), dk_ref), rel_l2(dv[0, keys, 3].cpu(), dv_ref)
+    log(f"full-size dK/dV sampled keys (head 3): rel L2 {ek:.3e} {ev:.3e}")
+    assert ek <= TOL_GRAD and ev <= TOL_GRAD
+    # identities on every head (GPU tensors, fp64 sums)
+    dks = dk.double().sum(dim=1)                       # [1, H, D]
+    scale = float(dk.double().abs().sum(dim=1).max())
+    assert float(dks.abs().max()) <= 1e-3 * scale
+    lhs = (dv.double() * vd.double()).sum(dim=(1, 3))
+    rhs = (dod.double() * out.double()).sum(dim=(1, 3))
+    rel = float(((lhs - rhs).abs() / rhs.abs().clamp_min(1e-6)).max())
+    log(f"identities: max|sum_j dK_j| / sum|dK| {float(dks.abs().max()) / scale:.3e}, <dV,V> vs <dO,O> rel {rel:.3e}")
+    assert rel <= 2e-2

@@ -415,3 +415,22 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     p, _ = oa._softmax_rows(s, allowed_mask(np.arange(S), np.arange(S)))
     ds_wrong = p * (dd[0, :, 0] @ vv[0, :, 0].T)
     assert np.abs((tau * ds_wrong.T @ qq[0, :, 0]).sum(axis=0)).max() > 1e-3
+
+
+# ---------------------------------------------------------------- sampled backward helpers
+
+@pytest.mark.parametrize("hq,hkv,s2", [(2, 2, None), (4, 2, None), (4, 4, S2Spec(8, 2, 32))])
+def test_sampled_backward_helpers_match_full(hq, hkv, s2):
+    from oracle import backward_delta, cols_backward_dkdv, rows_backward_dq
+    S, D = 32, 8
+    q, k, v, do = (_rand((1, S, h, D), s) for h, s in ((hq, 150), (hkv, 151), (hkv, 152), (hq, 153)))
+    dq, dk, dv, o, _ = attention_backward(q, k, v, do, s2=s2)
+    rows = [0, 3, 17, 31]
+    for h in range(hq):
+        np.testing.assert_allclose(rows_backward_dq(q, k, v, do, 0, h, rows, s2=s2), dq[0, rows, h], atol=1e-13)
+    keys = [0, 5, 30, 31]
+    for kh in range(hkv):
+        dks, dvs = cols_backward_dkdv(q, k, v, do, 0, kh, keys, s2=s2, row_block=7)
+        np.testing.assert_allclose(dks, dk[0, keys, kh], atol=1e-13)
+        np.testing.assert_allclose(dvs, dv[0, keys, kh], atol=1e-13)
+    np.testing.assert_allclose(backward_delta(o, do)[0, 0], np.sum(o[0, :, 0] * do[0, :, 0], axis=-1), atol=1e-14)
