@@ -10,7 +10,7 @@ import torch
 
 import long_context_exact_blockattn_amd as ba
 from long_context_exact_blockattn_amd import _lib
-from oracle import S2Spec, attention_backward, backward_delta, cols_backward_dkdv, rows_backward_dq
+from oracle import S2Spec, attention_backward, backward_delta, rows_backward_dq
 from tests.gpu_helpers import TOL_GRAD, dev, f64, log, rel_l2
 from workloads import chunk_order, get, make_inputs
 
@@ -118,11 +118,12 @@ def test_s2_backward_llama2_7b_s8k_heads_subset():
     _check_grads("s2 bwd S=8192 G=2048 heads {0,15,16,31}", got, ref)
 
 
-def test_backward_full_size_sampled():
-    """Training-step shape (S=65536, H=40, 8 ring chunks): sampled dQ rows, sampled dK/dV keys.
+def test_backward_full_size_one_head_and_sampled_rows():
+    """Training-step shape (S=65536, H=40, 8 ring chunks in seeded order).
 
-    Plus properties that hold at any size for every head: sum_j dK_j = 0 and
-    <dV, V> = <dO, O>.
+    One head (3) is checked in full against the oracle's backward of that head
+    (heads are independent in MHA); dQ rows of two more heads are sampled; on
+    every head <dV, V> = <dO, O> holds up to the bf16 storage of O.
     """
     w = get("llama2_13b_s64k_ring8_train")
     log("full-size backward: generating inputs")
@@ -139,19 +140,17 @@ def test_backward_full_size_sampled():
     for h in (0, w.heads_q - 1):
         ref = rows_backward_dq(qn, kn, vn, don, 0, h, rows)
         worst = max(worst, rel_l2(dq[0, rows, h].cpu(), ref))
-    log(f"full-size dQ sampled rows: rel L2 {worst:.3e}")
+    log(f"full-size dQ sampled rows (heads 0, {w.heads_q - 1}): rel L2 {worst:.3e}")
     assert worst <= TOL_GRAD
-    keys = sorted({0, 1, w.seqlen - 1, 8191, 8192, *map(int, rng.integers(0, w.seqlen, 6))})
-    dk_ref, dv_ref = cols_backward_dkdv(qn, kn, vn, don, 0, 3, keys, row_block=2048)
-    ek, ev = rel_l2(dk[0, keys, 3].cpu(), dk_ref), rel_l2(dv[0, keys, 3].cpu(), dv_ref)
-    log(f"full-size dK/dV sampled keys (head 3): rel L2 {ek:.3e} {ev:.3e}")
-    assert ek <= TOL_GRAD and ev <= TOL_GRAD
-    # identities on every head (GPU tensors, fp64 sums)
-    dks = dk.double().sum(dim=1)                       # [1, H, D]
-    scale = float(dk.double().abs().sum(dim=1).max())
-    assert float(dks.abs().max()) <= 1e-3 * scale
+    h = 3
+    log("full-size backward: oracle for head 3 (all rows, all keys)")
+    sl = lambda a: np.ascontiguousarray(a[:, :, h:h + 1])
+    ref = attention_backward(sl(qn), sl(kn), sl(vn), sl(don), row_block=1024)[:3]
+    got = (dq[:, :, h:h + 1], dk[:, :, h:h + 1], dv[:, :, h:h + 1])
+    _check_grads(f"full-size head {h} (S={w.seqlen}, {w.n_chunks} ring steps)", got, ref)
     lhs = (dv.double() * vd.double()).sum(dim=(1, 3))
     rhs = (dod.double() * out.double()).sum(dim=(1, 3))
-    rel = float(((lhs - rhs).abs() / rhs.abs().clamp_min(1e-6)).max())
-    log(f"identities: max|sum_j dK_j| / sum|dK| {float(dks.abs().max()) / scale:.3e}, <dV,V> vs <dO,O> rel {rel:.3e}")
-    assert rel <= 2e-2
+    norm = (dod.double() * out.double()).sum(dim=3).abs().sum(dim=1)
+    rel = float(((lhs - rhs).abs() / norm).max())
+    log(f"<dV,V> vs <dO,O> on every head: max |diff| / sum_i |dO_i.O_i| = {rel:.3e}")
+    assert rel <= 1e-2
