@@ -47,6 +47,36 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane L of the wave writes lds_base + 16*L, whatever global address it reads.
+// lds_base must be the same for every lane of the wave.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): this wave's outstanding vector-memory loads (including
+// direct-to-LDS ones) have landed.  expcnt and lgkmcnt are left unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 #endif
 
+// ---- LDS tile layout shared by every kernel --------------------------------
+// A tile is R rows x D bf16 with no padding; each row is D/8 chunks of 16
+// bytes and chunk c of row r is stored in slot c ^ swz(r).  The swizzle makes
+// both access patterns the kernels use conflict-free on the 64 LDS banks:
+//  - 16-byte reads of one chunk from 16 consecutive rows (MFMA operands whose
+//    contraction runs over D): swz is a bijection on r mod 16;
+//  - transposing 8-byte reads of 4 consecutive rows (from a multiple of 4) x
+//    4 aligned chunks (operands whose contraction runs over the rows): the
+//    high chunk bits of swz differ across the 4 rows.
+template <int D>
+BA_HD int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);  // D == 64: 8 chunks, 32 banks per row
+}
+
+// element offset of (row r, element e) inside a tile
+template <int D>
+BA_HD int tile_off(int r, int e) {
+  return r * D + ((((e >> 3) ^ swz<D>(r)) << 3) | (e & 7));
+}
 }  // namespace ba

@@ -2,10 +2,12 @@
 //
 // Work item = (batch, query head, tile of BM = 128 query rows); 4 waves, each
 // owning 32 query rows.  Key/value tiles of BN = 64 rows stream through a
-// double-buffered LDS ring; scores and outputs use v_mfma_f32_32x32x16_bf16 in
-// the TRANSPOSED form, S^T = K Q^T and O^T += V^T P^T, so that one lane holds
-// the scores of ONE query row: the row max and row sum of the online softmax
-// are in-lane reductions plus a single exchange between the two lane halves.
+// double-buffered LDS ring filled by direct global->LDS loads (no staging
+// registers); the tile loop is unrolled by two so both buffers sit at fixed
+// LDS addresses.  Scores and outputs use v_mfma_f32_32x32x16_bf16 in the
+// TRANSPOSED form, S^T = K Q^T and O^T += V^T P^T, so that one lane holds the
+// scores of ONE query row: the row max and row sum of the online softmax are
+// in-lane reductions plus a single exchange between the two lane halves.
 //
 // Online softmax (Milakov & Gimelshein's online normaliser, cited by the Ring
 // Attention summary's references): running max m and sum l per row, in base 2
@@ -47,17 +49,17 @@ template <int D>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int ROW = D + 8;            // padded LDS row (bf16 elements)
-  constexpr int CPR = D / 8;            // 16-byte chunks per row
-  constexpr int RPP = kFwdThreads / CPR;  // rows per load pass
-  constexpr int NPASS = BN / RPP;
-  constexpr int KK = D / 16;            // MFMA k-steps over D
-  constexpr int DB = D / 32;            // 32-wide blocks of D in the output
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * ROW];
+  constexpr int NW = kFwdThreads / 64;       // waves
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NPI = BN * CPR / (64 * NW);  // direct-load instructions per wave per tensor
+  constexpr int KK = D / 16;                 // MFMA k-steps over D
+  constexpr int DB = D / 32;                 // 32-wide blocks of D in the output
+  constexpr int TILE = BN * D;               // elements per tile
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0, V0, K1, V1 (swizzled)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;   // lane half
   const int l32 = lane & 31;
 
@@ -80,12 +82,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const int rloc = wave * 32 + l32;            // row within the tile
   const bool row_ok = rloc < qt.rows;
   const int64_t row = qt.row0 + rloc;          // original query row
-  const int64_t qcpos = qt.cpos0 + rloc;       // coordinate position of this lane's row
   const int64_t wave_cmin = qt.cpos0 + wave * 32;
   const int64_t wave_cmax = wave_cmin + 31;
-
-  const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
-  const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -103,117 +101,134 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         qf[kk] = row_ok ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
     }
 
-    // Next-tile staging through registers: K is fetched at the top of an
-    // iteration and written to the free LDS buffer after the score MFMAs; V is
-    // fetched then and written after the output MFMAs.
-    u32x4 st[NPASS];
-    auto gload = [&](const bf16* base, int64_t kt) {
-      const KTile t = make_ktile(sc, kt);
+    // ---- per-lane offsets, computed once
+    // K fragment (row l32 of a 32-key block, chunk 2kk+hl); the second block adds 32*D
+    int k_off[KK];
 #pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + tid / CPR;
-        const int c = tid % CPR;
-        st[p] = r < t.rows ? *(const u32x4*)(base + (t.row0 + r) * a.ks_s + 8 * c) : u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] = tile_off<D>(l32, 16 * kk + 8 * hl);
+    // V^T fragment, read transposed: rows k0 (+16kc) and k0 + 8 (+16kc), columns dcol
+    const int gi = lane & 15;
+    const int k0 = 4 * hl + (gi >> 2);
+    int v_off[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+      v_off[db][0] = tile_off<D>(k0, dcol);
+      v_off[db][1] = tile_off<D>(k0 + 8, dcol);
+    }
+    // direct loads: lane fills slot ci of the tile with row r, chunk c of the source
+    int g_row[NPI], g_col[NPI];
+#pragma unroll
+    for (int p = 0; p < NPI; ++p) {
+      const int ci = (p * NW + wave) * 64 + lane;
+      g_row[p] = ci / CPR;
+      g_col[p] = 8 * ((ci % CPR) ^ swz<D>(ci / CPR));
+    }
+    const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+    const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
+    const int ks_s = (int)a.ks_s;
+    // this lane's row, relative to the first row of its wave (for the mask)
+    const int64_t wave_rel0 = wave_cmin;
+
+    auto issue_tile = [&](bf16* kdst, bf16* vdst, int64_t kt) {
+      const KTile t = make_ktile(sc, kt);
+      const bf16* kt_base = kbase + t.row0 * a.ks_s;
+      const bf16* vt_base = vbase + t.row0 * a.ks_s;
+      const int last = (int)t.rows - 1;
+#pragma unroll
+      for (int p = 0; p < NPI; ++p) {
+        const int r = g_row[p] < last ? g_row[p] : last;  // ragged tail re-reads the last row
+        const unsigned off = (unsigned)(r * ks_s + g_col[p]);
+        g2lds16(kt_base + off, kdst + (p * NW + wave) * 512);
+        g2lds16(vt_base + off, vdst + (p * NW + wave) * 512);
       }
     };
-    auto lstore = [&](bf16* dst) {
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + tid / CPR;
-        const int c = tid % CPR;
-        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[p];
-      }
-    };
 
-    gload(kbase, qt.kt_begin);
-    lstore(smem[0][0]);
-    gload(vbase, qt.kt_begin);
-    lstore(smem[0][1]);
-    __syncthreads();
-
-    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; ++kt) {
-      const int buf = (int)((kt - qt.kt_begin) & 1);
-      const bool has_next = kt + 1 < qt.kt_end;
-      if (has_next) gload(kbase, kt + 1);
-
+    // one key tile from a fixed buffer
+    auto tile_step = [&](const bf16* Ks, const bf16* Vs, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
-      const bool wave_active = !(a.causal && t.cpos0 > wave_cmax);
-      if (wave_active) {
-        const bf16* Ks = smem[buf][0];
-        const bf16* Vs = smem[buf][1];
-        // ---- S^T = K Q^T  (two 32-key blocks)
-        f32x16 s[2];
+      if (a.causal && t.cpos0 > wave_cmax) return;  // every key after every row of this wave
+      // ---- S^T = K Q^T  (two 32-key blocks)
+      f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + k_off[0]), qf[0], f32x16{});
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 kf = *(const bf16x8*)(&Ks[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
-            s[kb] = mfma32(kf, qf[kk], s[kb]);
-          }
+        for (int kk = 1; kk < KK; ++kk)
+          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + k_off[kk]), qf[kk], s[kb]);
+      }
+      // ---- mask: keys past the chunk's end or (causal) after this lane's row
+      const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
+      if (need_mask) {
+        // last allowed key index of this lane's row, in 32 bits
+        int lim = (int)t.rows - 1;
+        if (a.causal) {
+          const int64_t c = wave_rel0 - t.cpos0;  // >= -31 here, < BN
+          const int cl = (int)c + l32;
+          lim = cl < lim ? cl : lim;
         }
-        if (has_next) {
-          lstore(smem[buf ^ 1][0]);
-          gload(vbase, kt + 1);
-        }
-        // ---- mask: ragged chunk tail, causal diagonal (coordinate positions)
-        const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-              const bool ok = key < t.rows && (!a.causal || t.cpos0 + key <= qcpos);
-              s[kb][r] = ok ? s[kb][r] : -INFINITY;
-            }
-        }
-        // ---- online softmax (base 2)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_hw(m_run - m_use);
-        float rsum = 0.f;
-        bf16x8 pf[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -m_use));
-            rsum += p;
-            pf[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            s[kb][r] = key <= lim ? s[kb][r] : -INFINITY;
           }
-        l_run = l_run * alpha + rsum;
-        m_run = m_new;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-        }
-        // ---- O^T += V^T P^T ; V^T operand read transposed from the natural [key][d] tile
-        const int gi = lane & 15;
-        const int dsub = 16 * ((lane >> 4) & 1);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            const int k0 = 16 * kc + 4 * hl + (gi >> 2);
-            const int dcol = 32 * db + dsub + 4 * (gi & 3);
-            const bf16x4 v0 = lds_read_tr16(&Vs[k0 * ROW + dcol]);
-            const bf16x4 v1 = lds_read_tr16(&Vs[(k0 + 8) * ROW + dcol]);
-            const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = mfma32(vf, pf[kc], oacc[db]);
-          }
-        }
-      } else if (has_next) {
-        lstore(smem[buf ^ 1][0]);
-        gload(vbase, kt + 1);
       }
-      if (has_next) lstore(smem[buf ^ 1][1]);
+      // ---- online softmax (base 2)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_hw(m_run - m_use);
+      float rsum = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -m_use));
+          rsum += p;
+          pf[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+        }
+      l_run = l_run * alpha + rsum;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      }
+      // ---- O^T += V^T P^T ; V^T operand read transposed from the [key][d] tile
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const bf16x4 v0 = lds_read_tr16(Vs + 16 * kc * D + v_off[db][0]);
+          const bf16x4 v1 = lds_read_tr16(Vs + 16 * kc * D + v_off[db][1]);
+          oacc[db] = mfma32(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), pf[kc], oacc[db]);
+        }
+      }
+    };
+
+    bf16* K0 = smem;
+    bf16* V0 = smem + TILE;
+    bf16* K1 = smem + 2 * TILE;
+    bf16* V1 = smem + 3 * TILE;
+    issue_tile(K0, V0, qt.kt_begin);
+    wait_vmem();
+    __syncthreads();
+    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; kt += 2) {
+      if (kt + 1 < qt.kt_end) issue_tile(K1, V1, kt + 1);
+      tile_step(K0, V0, kt);
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 >= qt.kt_end) break;
+      if (kt + 2 < qt.kt_end) issue_tile(K0, V0, kt + 2);
+      tile_step(K1, V1, kt + 1);
+      wait_vmem();
       __syncthreads();
     }
   }

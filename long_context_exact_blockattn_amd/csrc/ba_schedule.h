@@ -49,7 +49,7 @@ BA_HD QTile make_qtile(const Sched& s, int64_t qt) {
   QTile t;
   if (s.s2_group > 0) {
     const int64_t r0 = qt * s.BM;  // rolled position of the first query
-    t.row0 = (r0 + s.s2_shift) % s.Sq;
+    t.row0 = r0 + s.s2_shift >= s.Sq ? r0 + s.s2_shift - s.Sq : r0 + s.s2_shift;
     t.rows = s.BM;
     t.cpos0 = r0;
     const int64_t g0 = (r0 / s.s2_group) * s.s2_group;
@@ -76,7 +76,7 @@ BA_HD KTile make_ktile(const Sched& s, int64_t kt) {
   KTile k;
   if (s.s2_group > 0) {
     const int64_t r0 = kt * s.BN;
-    k.row0 = (r0 + s.s2_shift) % s.Sk;
+    k.row0 = r0 + s.s2_shift >= s.Sk ? r0 + s.s2_shift - s.Sk : r0 + s.s2_shift;
     k.rows = s.BN;
     k.cpos0 = r0;
     return k;
@@ -113,7 +113,7 @@ BA_HD KVItem make_kv_item(const Sched& s, int64_t kt) {
   const int64_t nq = num_qtiles(s);
   if (s.s2_group > 0) {
     const int64_t r0 = kt * s.BN;
-    it.krow0 = (r0 + s.s2_shift) % s.Sk;
+    it.krow0 = r0 + s.s2_shift >= s.Sk ? r0 + s.s2_shift - s.Sk : r0 + s.s2_shift;
     it.krows = s.BN;
     it.kcpos0 = r0;
     const int64_t gend = (r0 / s.s2_group + 1) * s.s2_group;  // end of the key's group (rolled)
