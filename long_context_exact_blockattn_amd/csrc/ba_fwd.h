@@ -11,8 +11,9 @@
 //
 // Online softmax (Milakov & Gimelshein's online normaliser, cited by the Ring
 // Attention summary's references): running max m and sum l per row, in base 2
-// with tau*log2(e) folded into one FMA; a fully masked row keeps m = -inf and
-// l = 0 without producing NaN.  The epilogue turns (acc, m, l) into the
+// with tau*log2(e) folded into one FMA; m is only raised when a tile's max
+// exceeds it by more than 2^8, so the O rescale is rare; a fully masked row
+// keeps m = -inf and l = 0 without producing NaN.  The epilogue turns (acc, m, l) into the
 // chunk's partial pair and, in ACCUMULATE mode, merges it into the running
 // pair (O_acc, LSE_acc) in fp32 -- the order-independent combination of the
 // Ring Attention summary (Summary).
@@ -163,7 +164,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
         // last allowed key index of this lane's row, in 32 bits
         int lim = (int)t.rows - 1;
         if (a.causal) {
-          const int64_t c = wave_rel0 - t.cpos0;  // >= -31 here, < BN
+          int64_t c = wave_rel0 - t.cpos0;  // >= -31 for an active wave
+          c = c > BN ? BN : c;
           const int cl = (int)c + l32;
           lim = cl < lim ? cl : lim;
         }
@@ -182,7 +184,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      // The running max moves only when a tile's max exceeds it by more than 8
+      // (base 2): p = 2^(s - m) then stays <= 256, exact in fp32 sums and in
+      // bf16's range, and the O rescale below is skipped on almost every tile.
+      const float mx2 = mx * a.scale_log2;
+      const float m_new = (mx2 > m_run + 8.f) ? mx2 : m_run;
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_hw(m_run - m_use);
       float rsum = 0.f;
