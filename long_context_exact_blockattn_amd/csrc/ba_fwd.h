@@ -42,14 +42,21 @@ struct FwdArgs {
   int64_t n_items;
 };
 
-constexpr int kFwdBM = 128;
-constexpr int kFwdBN = 64;
+// Query blocks of 32 rows per wave: with two, every K or V fragment read from
+// LDS feeds two MFMAs (LDS read bandwidth caps a one-block design), at one
+// wave per SIMD.
+#ifndef BA_FWD_QB
+#define BA_FWD_QB 1
+#endif
+constexpr int kFwdQB = BA_FWD_QB;
 constexpr int kFwdThreads = 256;
+constexpr int kFwdBM = (kFwdThreads / 64) * 32 * kFwdQB;
+constexpr int kFwdBN = 64;
 
 template <int D>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int BM = kFwdBM, BN = kFwdBN, QB = kFwdQB;
   constexpr int NW = kFwdThreads / 64;       // waves
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int NPI = BN * CPR / (64 * NW);  // direct-load instructions per wave per tensor
@@ -80,26 +87,32 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const bool empty = qt.kt_end <= qt.kt_begin;
   if (empty && a.accumulate && a.o_final == nullptr) return;
 
-  const int rloc = wave * 32 + l32;            // row within the tile
-  const bool row_ok = rloc < qt.rows;
-  const int64_t row = qt.row0 + rloc;          // original query row
-  const int64_t wave_cmin = qt.cpos0 + wave * 32;
-  const int64_t wave_cmax = wave_cmin + 31;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x16 oacc[DB];
+  // rows of this lane: block qb holds tile row wave*32*QB + qb*32 + l32
+  int rloc[QB];
+  bool row_ok[QB];
+  float m_run[QB], l_run[QB];
+  f32x16 oacc[QB][DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) {
+    rloc[qb] = wave * 32 * QB + qb * 32 + l32;
+    row_ok[qb] = rloc[qb] < qt.rows;
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[qb][i] = f32x16{};
+  }
+  const int64_t wave_cmin = qt.cpos0 + wave * 32 * QB;  // coordinate of the wave's first row
+  const int64_t wave_cmax = wave_cmin + 32 * QB - 1;
 
   if (!empty) {
     // ---- resident query fragments: B operand of S^T = K Q^T
-    bf16x8 qf[KK];
-    {
-      const bf16* qp = a.q + (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 8 * hl;
+    bf16x8 qf[QB][KK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const bf16* qp = a.q + (int64_t)b * a.qs_b + (qt.row0 + rloc[qb]) * a.qs_s + (int64_t)h * a.qs_h + 8 * hl;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        qf[kk] = row_ok ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
+        qf[qb][kk] = row_ok[qb] ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
     }
 
     // ---- per-lane offsets, computed once
@@ -128,8 +141,6 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
     const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
     const int ks_s = (int)a.ks_s;
-    // this lane's row, relative to the first row of its wave (for the mask)
-    const int64_t wave_rel0 = wave_cmin;
 
     auto issue_tile = [&](bf16* kdst, bf16* vdst, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
@@ -149,72 +160,85 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     auto tile_step = [&](const bf16* Ks, const bf16* Vs, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
       if (a.causal && t.cpos0 > wave_cmax) return;  // every key after every row of this wave
-      // ---- S^T = K Q^T  (two 32-key blocks)
-      f32x16 s[2];
+      // ---- S^T = K Q^T  (two 32-key blocks; each K fragment feeds QB MFMAs)
+      f32x16 s[QB][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + k_off[0]), qf[0], f32x16{});
 #pragma unroll
-        for (int kk = 1; kk < KK; ++kk)
-          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + k_off[kk]), qf[kk], s[kb]);
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 kf = *(const bf16x8*)(Ks + kb * 32 * D + k_off[kk]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][kb] = mfma32(kf, qf[qb][kk], kk == 0 ? f32x16{} : s[qb][kb]);
+        }
       }
       // ---- mask: keys past the chunk's end or (causal) after this lane's row
       const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
       if (need_mask) {
-        // last allowed key index of this lane's row, in 32 bits
-        int lim = (int)t.rows - 1;
-        if (a.causal) {
-          int64_t c = wave_rel0 - t.cpos0;  // >= -31 for an active wave
-          c = c > BN ? BN : c;
-          const int cl = (int)c + l32;
-          lim = cl < lim ? cl : lim;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          // last allowed key index of this lane's row in block qb, in 32 bits
+          int lim = (int)t.rows - 1;
+          if (a.causal) {
+            int64_t c = wave_cmin + 32 * qb - t.cpos0;  // >= -32*QB for an active wave
+            c = c > BN ? BN : c;
+            const int cl = (int)c + l32;
+            lim = cl < lim ? cl : lim;
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+              s[qb][kb][r] = key <= lim ? s[qb][kb][r] : -INFINITY;
+            }
         }
+      }
+      // ---- online softmax (base 2), per query block
+      bf16x8 pf[QB][4];
+      float alpha[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        // The running max moves only when a tile's max exceeds it by more than 8
+        // (base 2): p = 2^(s - m) then stays <= 256, exact in fp32 sums and in
+        // bf16's range, and the O rescale below is skipped on almost every tile.
+        const float mx2 = mx * a.scale_log2;
+        const float m_new = (mx2 > m_run[qb] + 8.f) ? mx2 : m_run[qb];
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha[qb] = exp2_hw(m_run[qb] - m_use);
+        float rsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            s[kb][r] = key <= lim ? s[kb][r] : -INFINITY;
+            const float p = exp2_hw(__builtin_fmaf(s[qb][kb][r], a.scale_log2, -m_use));
+            rsum += p;
+            pf[qb][kb * 2 + (r >> 3)][r & 7] = (bf16)p;
           }
-      }
-      // ---- online softmax (base 2)
-      float mx = -INFINITY;
+        l_run[qb] = l_run[qb] * alpha[qb] + rsum;
+        m_run[qb] = m_new;
+        if (__any(alpha[qb] != 1.f)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      // The running max moves only when a tile's max exceeds it by more than 8
-      // (base 2): p = 2^(s - m) then stays <= 256, exact in fp32 sums and in
-      // bf16's range, and the O rescale below is skipped on almost every tile.
-      const float mx2 = mx * a.scale_log2;
-      const float m_new = (mx2 > m_run + 8.f) ? mx2 : m_run;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run - m_use);
-      float rsum = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -m_use));
-          rsum += p;
-          pf[kb * 2 + (r >> 3)][r & 7] = (bf16)p;
+          for (int i = 0; i < DB; ++i) oacc[qb][i] *= alpha[qb];
         }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       }
-      // ---- O^T += V^T P^T ; V^T operand read transposed from the [key][d] tile
+      // ---- O^T += V^T P^T ; V^T operand read transposed from the [key][d] tile,
+      // each fragment feeding QB MFMAs
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           const bf16x4 v0 = lds_read_tr16(Vs + 16 * kc * D + v_off[db][0]);
           const bf16x4 v1 = lds_read_tr16(Vs + 16 * kc * D + v_off[db][1]);
-          oacc[db] = mfma32(__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), pf[kc], oacc[db]);
+          const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32(vf, pf[qb][kc], oacc[qb][db]);
         }
       }
     };
@@ -239,63 +263,66 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // ---- epilogue: partial pair of this chunk, optional merge into the running pair
-  const float l_tot = l_run + wave_xor32(l_run);
-  const bool has = l_tot > 0.f;
-  const float lse2_c = has ? m_run + log2_hw(l_tot) : -INFINITY;
-  const float inv_l = has ? 1.f / l_tot : 0.f;
-  if (!row_ok) return;
-
-  const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
-  const int64_t obase = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 4 * hl;
-  float ca = 0.f, cc = inv_l, L2 = lse2_c;
-  if (a.accumulate) {
-    const float la2 = a.lse[lse_idx] * kLog2e;
-    const float M = fmaxf(la2, lse2_c);
-    if (M == -INFINITY) {
-      ca = 0.f; cc = 0.f; L2 = -INFINITY;
-    } else {
-      const float wa = exp2_hw(la2 - M);
-      const float wc = exp2_hw(lse2_c - M);
-      const float tot = wa + wc;
-      L2 = M + log2_hw(tot);
-      ca = wa / tot;
-      cc = wc / tot * inv_l;
-    }
-  }
-  const bool write_state = !(a.accumulate && empty);
+  // ---- epilogue, per query block: partial pair of this chunk, optional merge
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t off = obase + 32 * db + 8 * g;
-      f32x4 val;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = cc * oacc[db][4 * g + e];
-      if (a.accumulate && ca > 0.f) {
-        const f32x4 prev = *(const f32x4*)((const float*)a.o + off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(ca, prev[e], val[e]);
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + wave_xor32(l_run[qb]);
+    const bool has = l_tot > 0.f;
+    const float lse2_c = has ? m_run[qb] + log2_hw(l_tot) : -INFINITY;
+    const float inv_l = has ? 1.f / l_tot : 0.f;
+    if (!row_ok[qb]) continue;
+    const int64_t row = qt.row0 + rloc[qb];
+    const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
+    const int64_t obase = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 4 * hl;
+    float ca = 0.f, cc = inv_l, L2 = lse2_c;
+    if (a.accumulate) {
+      const float la2 = a.lse[lse_idx] * kLog2e;
+      const float M = fmaxf(la2, lse2_c);
+      if (M == -INFINITY) {
+        ca = 0.f; cc = 0.f; L2 = -INFINITY;
+      } else {
+        const float wa = exp2_hw(la2 - M);
+        const float wc = exp2_hw(lse2_c - M);
+        const float tot = wa + wc;
+        L2 = M + log2_hw(tot);
+        ca = wa / tot;
+        cc = wc / tot * inv_l;
       }
-      if (write_state) {
-        if (a.o_f32) {
-          *(f32x4*)((float*)a.o + off) = val;
-        } else {
+    }
+    const bool write_state = !(a.accumulate && empty);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t off = obase + 32 * db + 8 * g;
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = cc * oacc[qb][db][4 * g + e];
+        if (a.accumulate && ca > 0.f) {
+          const f32x4 prev = *(const f32x4*)((const float*)a.o + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(ca, prev[e], val[e]);
+        }
+        if (write_state) {
+          if (a.o_f32) {
+            *(f32x4*)((float*)a.o + off) = val;
+          } else {
+            bf16x4 bv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
+            *(bf16x4*)((bf16*)a.o + off) = bv;
+          }
+        }
+        if (a.o_final) {
           bf16x4 bv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
-          *(bf16x4*)((bf16*)a.o + off) = bv;
+          *(bf16x4*)(a.o_final + off) = bv;
         }
       }
-      if (a.o_final) {
-        bf16x4 bv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
-        *(bf16x4*)(a.o_final + off) = bv;
-      }
     }
+    if (write_state && hl == 0) a.lse[lse_idx] = L2 * kLn2;
   }
-  if (write_state && hl == 0) a.lse[lse_idx] = L2 * kLn2;
 #endif
 }
 
