@@ -91,6 +91,82 @@ def run_ring_forward(w, steps, warmup):
             "kernel": "fwd_kernel<128>", "src": FWD_SRC}
 
 
+def run_training(w, steps, warmup):
+    """Ring forward + ring backward (training step of attention), or S2 forward + backward."""
+    import torch
+
+    import long_context_exact_blockattn_amd as ba
+    from long_context_exact_blockattn_amd import _lib
+    from workloads import chunk_bounds, chunk_order, make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
+    q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    b, s, hq, d = q.shape
+    if w.s2_group is not None:
+        o = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
+        lse = torch.empty(b, hq, s, device=dev)
+        delta = torch.empty(b, hq, s, device=dev)
+        dq_acc = torch.empty(b, s, hq, d, device=dev)
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+
+        def fwd():
+            _lib.s2attn_fwd(q, k, v, o, lse, group=w.s2_group, shift_head0=w.s2_shift_head0)
+
+        def bwd():
+            dq_acc.zero_()
+            _lib.s2attn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, group=w.s2_group,
+                            shift_head0=w.s2_shift_head0, dq_final=dq,
+                            flags=_lib.BA_BWD_COMPUTE_DELTA | _lib.BA_BWD_FINALIZE_DQ)
+        order = None
+    else:
+        order = chunk_order(w.n_chunks, seed=w.seed)
+        bounds = chunk_bounds(w.seqlen, w.n_chunks)
+        o_acc = torch.empty(b, s, hq, d, device=dev)
+        lse = torch.empty(b, hq, s, device=dev)
+        o = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
+        delta = torch.empty(b, hq, s, device=dev)
+        dq_acc = torch.empty(b, s, hq, d, device=dev)
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        n = len(order)
+
+        def fwd():
+            for t, c in enumerate(order):
+                c0, c1 = bounds[c]
+                _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
+                                   mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
+                                   o_final=o if t == n - 1 else None, k_pos0=c0)
+
+        def bwd():
+            dq_acc.zero_()
+            for t, c in enumerate(order):
+                c0, c1 = bounds[c]
+                flags = (_lib.BA_BWD_COMPUTE_DELTA if t == 0 else 0) | (_lib.BA_BWD_FINALIZE_DQ if t == n - 1 else 0)
+                _lib.blockattn_bwd(q, k[:, c0:c1], v[:, c0:c1], o, do, lse, delta, dq_acc,
+                                   dk[:, c0:c1], dv[:, c0:c1], dq_final=dq, flags=flags, k_pos0=c0)
+
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(warmup):
+        fwd(); bwd()
+    torch.cuda.synchronize()
+    fwd_ms, bwd_ms = [], []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for _ in range(steps):
+        pass
+    fwd_ms = e[0].elapsed_time(e[1])
+    bwd_ms = e[1].elapsed_time(e[2])
+    assert not torch.isnan(dq).any() and not torch.isnan(dk).any(), "NaN in gradients"
+    return {"wall_s": wall, "fwd_ms_last": fwd_ms, "bwd_ms_last": bwd_ms, "order": order}
+
+
 def cpu_baseline(w, budget_heads=1):
     """The oracle as it stands, on one query head of the same workload (all ring steps)."""
     import numpy as np
@@ -131,6 +207,28 @@ def copy_calibration(reps):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": max(reps, 1)}), flush=True)
 
 
+def training_line(w, args):
+    """One JSON line for a forward+backward workload (attention training step)."""
+    r = run_training(w, args.steps, args.warmup)
+    ms = r["wall_s"] * 1e3 / args.steps
+    flop = w.fwd_flop() + w.bwd_flop()
+    tflops = flop / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks,
+                   "s2_group": w.s2_group, "chunk_order": r["order"], "phases": "forward+backward",
+                   "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                   "fwd_ms": round(r["fwd_ms_last"], 4), "bwd_ms": round(r["bwd_ms_last"], 4),
+                   "fwd_tflops": round(w.fwd_flop() / r["fwd_ms_last"] / 1e9, 2),
+                   "bwd_tflops": round(w.bwd_flop() / r["bwd_ms_last"] / 1e9, 2)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,8 +250,8 @@ def main():
     from workloads import get
     w = get(args.workload)
     if w.s2_group is not None or w.backward:
-        print(f"workload {w.name} is not a forward ring workload; use a forward ring workload", file=sys.stderr)
-        sys.exit(2)
+        training_line(w, args)
+        return
     r = run_ring_forward(w, args.steps, args.warmup)
     ms_per_step = r["wall_s"] * 1e3 / args.steps
     flop = w.fwd_flop()
