@@ -14,9 +14,10 @@
 //                 dQ over the key tiles the mask allows, then dq_acc += tau dQ
 // Every MFMA is v_mfma_f32_32x32x16_bf16 with operands arranged as in the
 // forward kernel (see ba_fwd.h): the stationary side is the B operand held in
-// registers, tiles of the streamed side are read from LDS, directly for
-// contractions over D and through ds_read_b64_tr_b16 for contractions over
-// the streamed rows.
+// registers; tiles of the streamed side sit in the swizzled LDS layout of
+// ba_common.h, filled by direct global->LDS loads and read directly for
+// contractions over D, through ds_read_b64_tr_b16 for contractions over the
+// streamed rows.
 #pragma once
 
 #include "ba_common.h"
@@ -62,6 +63,49 @@ __device__ __forceinline__ Sched bwd_sched(const BwdArgs& a, int head, int BM, i
   return sc;
 }
 
+// Direct loads of one R-row tile into the swizzled LDS layout: slot ci of the
+// tile gets row ci / CPR, chunk (ci % CPR) ^ swz(row) of the source.  Rows past
+// the end of a ragged tile re-read its last valid row (masked by the caller).
+template <int D, int R>
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int NW = kBwdThreads / 64;
+  static constexpr int NPI = R * CPR / (64 * NW);
+  static constexpr int STEP = 64 * NW / CPR;  // rows between consecutive instructions
+  // Slot ci = (p*NW + wave)*64 + lane is row ci / CPR = row0 + p*STEP; the row's
+  // swizzle depends on row mod 16 only and STEP is a multiple of 16, so the
+  // source chunk is the same for every instruction.
+  int row0, col;
+  __device__ __forceinline__ void init(int wave, int lane) {
+    const int ci = wave * 64 + lane;
+    row0 = ci / CPR;
+    col = 8 * ((ci % CPR) ^ swz<D>(row0));
+  }
+  // src points at row 0 of the tile; rows are `stride` elements apart
+  __device__ __forceinline__ void issue(const bf16* src, int stride, int rows, bf16* dst, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int last = rows - 1;
+#pragma unroll
+    for (int p = 0; p < NPI; ++p) {
+      int r = row0 + p * STEP;
+      r = r < last ? r : last;
+      g2lds16(src + (unsigned)(r * stride + col), dst + (p * NW + wave) * 512);
+    }
+#endif
+  }
+};
+static_assert(TileLoader<128, 64>::STEP % 16 == 0 && TileLoader<64, 64>::STEP % 16 == 0,
+              "the loader assumes the swizzle repeats every STEP rows");
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// bf16x8 MFMA operand from two transposing 8-byte LDS reads
+__device__ __forceinline__ bf16x8 tr_pair(const bf16* base, int off0, int off1) {
+  const bf16x4 x0 = lds_read_tr16(base + off0);
+  const bf16x4 x1 = lds_read_tr16(base + off1);
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+#endif
+
 // ---------------------------------------------------------------- delta = rowsum(dO * O)
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t n_threads) {
@@ -95,15 +139,13 @@ template <int D>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = kDqBM, BN = kDqBN;
-  constexpr int ROW = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int RPP = kBwdThreads / CPR;
-  constexpr int NPASS = BN / RPP;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2][2][BN * ROW];
+  constexpr int TILE = BN * D;
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0, V0, K1, V1 (swizzled)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
@@ -120,7 +162,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int rloc = wave * 32 + l32;
   const bool row_ok = rloc < qt.rows;
   const int64_t row = qt.row0 + rloc;
-  const int64_t qcpos = qt.cpos0 + rloc;
   const int64_t wave_cmin = qt.cpos0 + wave * 32;
   const int64_t wave_cmax = wave_cmin + 31;
   const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
@@ -139,84 +180,87 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       qf[kk] = row_ok ? *(const bf16x8*)(a.q + qoff + 16 * kk + 8 * hl) : bf16x8{};
       df[kk] = row_ok ? *(const bf16x8*)(a.dout + qoff + 16 * kk + 8 * hl) : bf16x8{};
     }
+    // per-lane LDS offsets: direct reads (row l32, chunk 2kk+hl) and transposed reads
+    int n_off[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) n_off[kk] = tile_off<D>(l32, 16 * kk + 8 * hl);
+    const int gi = lane & 15;
+    const int r0 = 4 * hl + (gi >> 2);
+    int t_off[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+      t_off[db][0] = tile_off<D>(r0, dcol);
+      t_off[db][1] = tile_off<D>(r0 + 8, dcol);
+    }
+    TileLoader<D, BN> ld;
+    ld.init(wave, lane);
     const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
     const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
-    u32x4 st[NPASS];
-    auto gload = [&](const bf16* base, int64_t kt) {
+    const int ks_s = (int)a.ks_s;
+    auto issue = [&](bf16* kd, bf16* vd, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + tid / CPR;
-        const int c = tid % CPR;
-        st[p] = r < t.rows ? *(const u32x4*)(base + (t.row0 + r) * a.ks_s + 8 * c) : u32x4{0, 0, 0, 0};
-      }
+      ld.issue(kbase + t.row0 * a.ks_s, ks_s, (int)t.rows, kd, wave);
+      ld.issue(vbase + t.row0 * a.ks_s, ks_s, (int)t.rows, vd, wave);
     };
-    auto lstore = [&](bf16* dst) {
-#pragma unroll
-      for (int p = 0; p < NPASS; ++p) {
-        const int r = p * RPP + tid / CPR;
-        const int c = tid % CPR;
-        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[p];
-      }
-    };
-    gload(kbase, qt.kt_begin);
-    lstore(smem[0][0]);
-    gload(vbase, qt.kt_begin);
-    lstore(smem[0][1]);
-    __syncthreads();
 
-    const int gi = lane & 15;
-    const int dsub = 16 * ((lane >> 4) & 1);
-    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; ++kt) {
-      const int buf = (int)((kt - qt.kt_begin) & 1);
-      const bool has_next = kt + 1 < qt.kt_end;
-      if (has_next) gload(kbase, kt + 1);
+    auto tile_step = [&](const bf16* Ks, const bf16* Vs, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
-      const bf16* Ks = smem[buf][0];
-      const bf16* Vs = smem[buf][1];
-      const bool active = !(a.causal && t.cpos0 > wave_cmax);
+      if (a.causal && t.cpos0 > wave_cmax) return;  // every key after every row of this wave
       const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
+      int lim = BN;
+      if (need_mask) {
+        lim = (int)t.rows - 1;
+        if (a.causal) {
+          int64_t c = wave_cmin - t.cpos0;
+          c = c > BN ? BN : c;
+          const int cl = (int)c + l32;
+          lim = cl < lim ? cl : lim;
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (kb == 1 && has_next) {
-          lstore(smem[buf ^ 1][0]);
-          gload(vbase, kt + 1);
-        }
-        if (!active) continue;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s, dp;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf = *(const bf16x8*)(&Ks[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
-          s = mfma32(kf, qf[kk], s);
-          const bf16x8 vf = *(const bf16x8*)(&Vs[(kb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
-          dp = mfma32(vf, df[kk], dp);
+          s = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + n_off[kk]), qf[kk], kk == 0 ? f32x16{} : s);
+          dp = mfma32(*(const bf16x8*)(Vs + kb * 32 * D + n_off[kk]), df[kk], kk == 0 ? f32x16{} : dp);
         }
         bf16x8 dsf[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
           float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -lse2));
-          if (need_mask) {
-            const bool ok = key < t.rows && (!a.causal || t.cpos0 + key <= qcpos);
-            p = ok ? p : 0.f;
-          }
+          if (need_mask) p = key <= lim ? p : 0.f;
           dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dlt));
         }
         // dQ^T += K^T dS^T: K^T operand read transposed from the [key][d] tile
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            const int k0 = kb * 32 + 16 * c2 + 4 * hl + (gi >> 2);
-            const int dcol = 32 * db + dsub + 4 * (gi & 3);
-            const bf16x4 x0 = lds_read_tr16(&Ks[k0 * ROW + dcol]);
-            const bf16x4 x1 = lds_read_tr16(&Ks[(k0 + 8) * ROW + dcol]);
-            const bf16x8 kt_op = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-            dqacc[db] = mfma32(kt_op, dsf[c2], dqacc[db]);
+            const bf16* base = Ks + (kb * 32 + 16 * c2) * D;
+            dqacc[db] = mfma32(tr_pair(base, t_off[db][0], t_off[db][1]), dsf[c2], dqacc[db]);
           }
-        }
       }
-      if (has_next) lstore(smem[buf ^ 1][1]);
+    };
+
+    bf16* K0 = smem;
+    bf16* V0 = smem + TILE;
+    bf16* K1 = smem + 2 * TILE;
+    bf16* V1 = smem + 3 * TILE;
+    issue(K0, V0, qt.kt_begin);
+    wait_vmem();
+    __syncthreads();
+    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; kt += 2) {
+      if (kt + 1 < qt.kt_end) issue(K1, V1, kt + 1);
+      tile_step(K0, V0, kt);
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 >= qt.kt_end) break;
+      if (kt + 2 < qt.kt_end) issue(K0, V0, kt + 2);
+      tile_step(K1, V1, kt + 1);
+      wait_vmem();
       __syncthreads();
     }
   }
@@ -250,18 +294,14 @@ template <int D>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = kKvBM, BN = kKvBN;
-  constexpr int ROW = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int RPP = kBwdThreads / CPR;
-  constexpr int NPASS = BM / RPP;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 qs[2][BM * ROW];
-  __shared__ __attribute__((aligned(16))) bf16 dos[2][BM * ROW];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BM];
-  __shared__ __attribute__((aligned(16))) float del_s[2][BM];
+  constexpr int TILE = BM * D;
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // Q0, dO0, Q1, dO1 (swizzled)
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse*log2e, delta][row]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
@@ -294,109 +334,116 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t nqt = it.qt_end > it.qt_begin ? it.qt_end - it.qt_begin : 0;
   const int64_t n_iter = nqt * a.grp;
   if (n_iter > 0) {
-    u32x4 st[NPASS];
+    int n_off[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) n_off[kk] = tile_off<D>(l32, 16 * kk + 8 * hl);
+    const int gi = lane & 15;
+    const int r0 = 4 * hl + (gi >> 2);
+    int t_off[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int dcol = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+      t_off[db][0] = tile_off<D>(r0, dcol);
+      t_off[db][1] = tile_off<D>(r0 + 8, dcol);
+    }
+    TileLoader<D, BM> ld;
+    ld.init(wave, lane);
+    const int qs_s = (int)a.qs_s;
     auto tile_of = [&](int64_t i, int* head, QTile* t) {
       *head = h0 + (int)(i / nqt);
       *t = make_qtile(sc, it.qt_begin + i % nqt);
     };
-    auto gload = [&](const bf16* base, int64_t i) {
+    // stage tile i: Q and dO by direct loads, LSE (base 2) and delta by ordinary loads
+    float st_l = INFINITY, st_d = 0.f;
+    auto issue = [&](bf16* qd, bf16* dd, int64_t i) {
       int hh; QTile t; tile_of(i, &hh, &t);
-      const bf16* p = base + (int64_t)b * a.qs_b + (int64_t)hh * a.qs_h;
-#pragma unroll
-      for (int pp = 0; pp < NPASS; ++pp) {
-        const int r = pp * RPP + tid / CPR;
-        const int c = tid % CPR;
-        st[pp] = r < t.rows ? *(const u32x4*)(p + (t.row0 + r) * a.qs_s + 8 * c) : u32x4{0, 0, 0, 0};
-      }
-    };
-    auto lstore = [&](bf16* dst) {
-#pragma unroll
-      for (int pp = 0; pp < NPASS; ++pp) {
-        const int r = pp * RPP + tid / CPR;
-        const int c = tid % CPR;
-        *(u32x4*)(&dst[r * ROW + 8 * c]) = st[pp];
-      }
-    };
-    auto stats = [&](int64_t i, int buf) {
+      const int64_t base = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
+      ld.issue(a.q + base, qs_s, (int)t.rows, qd, wave);
+      ld.issue(a.dout + base, qs_s, (int)t.rows, dd, wave);
       if (tid < BM) {
-        int hh; QTile t; tile_of(i, &hh, &t);
         const bool ok = tid < t.rows;
         const int64_t li = ((int64_t)b * a.Hq + hh) * a.Sq + t.row0 + tid;
-        lse_s[buf][tid] = ok ? a.lse[li] * kLog2e : INFINITY;
-        del_s[buf][tid] = ok ? a.delta[li] : 0.f;
+        st_l = ok ? a.lse[li] * kLog2e : INFINITY;
+        st_d = ok ? a.delta[li] : 0.f;
       }
     };
-    gload(a.q, 0);
-    lstore(qs[0]);
-    gload(a.dout, 0);
-    lstore(dos[0]);
-    stats(0, 0);
-    __syncthreads();
+    auto put_stats = [&](int buf) {
+      if (tid < BM) {
+        stat[buf][0][tid] = st_l;
+        stat[buf][1][tid] = st_d;
+      }
+    };
 
-    const int gi = lane & 15;
-    const int dsub = 16 * ((lane >> 4) & 1);
-    for (int64_t i = 0; i < n_iter; ++i) {
-      const int buf = (int)(i & 1);
-      const bool has_next = i + 1 < n_iter;
-      if (has_next) gload(a.q, i + 1);
+    auto tile_step = [&](const bf16* Qs, const bf16* Ds, const float* lse_s, const float* del_s, int64_t i) {
       int hh; QTile t; tile_of(i, &hh, &t);
-      const bf16* Qs = qs[buf];
-      const bf16* Ds = dos[buf];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        if (qb == 1 && has_next) {
-          lstore(qs[buf ^ 1]);
-          gload(a.dout, i + 1);
-        }
         const int64_t qc0 = t.cpos0 + qb * 32;
         if (a.causal && wave_kmin > qc0 + 31) continue;  // every pair of the block is masked
         const bool need_mask = (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > qc0);
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
+        int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
+        if (need_mask) {
+          if (!key_ok) {
+            qmin = 64;
+          } else if (a.causal) {
+            int64_t c = kcpos - qc0;
+            c = c < -1 ? -1 : (c > 64 ? 64 : c);
+            qmin = (int)c;
+          }
+        }
+        f32x16 s, dp;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 qa = *(const bf16x8*)(&Qs[(qb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
-          s = mfma32(qa, kf[kk], s);
-          const bf16x8 da = *(const bf16x8*)(&Ds[(qb * 32 + l32) * ROW + 16 * kk + 8 * hl]);
-          dp = mfma32(da, vf[kk], dp);
+          s = mfma32(*(const bf16x8*)(Qs + qb * 32 * D + n_off[kk]), kf[kk], kk == 0 ? f32x16{} : s);
+          dp = mfma32(*(const bf16x8*)(Ds + qb * 32 * D + n_off[kk]), vf[kk], kk == 0 ? f32x16{} : dp);
         }
         bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int q4 = qb * 32 + 8 * g + 4 * hl;
-          const f32x4 l4 = *(const f32x4*)(&lse_s[buf][q4]);
-          const f32x4 d4 = *(const f32x4*)(&del_s[buf][q4]);
+          const f32x4 l4 = *(const f32x4*)(lse_s + q4);
+          const f32x4 d4 = *(const f32x4*)(del_s + q4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -l4[e]));
-            if (need_mask) {
-              const bool ok = key_ok && (!a.causal || kcpos <= qc0 + 8 * g + 4 * hl + e);
-              p = ok ? p : 0.f;
-            }
+            if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
             pf[r >> 3][r & 7] = (bf16)p;
             dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - d4[e]));
           }
         }
         // dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            const int q0 = qb * 32 + 16 * c2 + 4 * hl + (gi >> 2);
-            const int dcol = 32 * db + dsub + 4 * (gi & 3);
-            const bf16x4 y0 = lds_read_tr16(&Ds[q0 * ROW + dcol]);
-            const bf16x4 y1 = lds_read_tr16(&Ds[(q0 + 8) * ROW + dcol]);
-            dvacc[db] = mfma32(__builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7), pf[c2], dvacc[db]);
-            const bf16x4 x0 = lds_read_tr16(&Qs[q0 * ROW + dcol]);
-            const bf16x4 x1 = lds_read_tr16(&Qs[(q0 + 8) * ROW + dcol]);
-            dkacc[db] = mfma32(__builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7), dsf[c2], dkacc[db]);
+            const int rb = (qb * 32 + 16 * c2) * D;
+            dvacc[db] = mfma32(tr_pair(Ds + rb, t_off[db][0], t_off[db][1]), pf[c2], dvacc[db]);
+            dkacc[db] = mfma32(tr_pair(Qs + rb, t_off[db][0], t_off[db][1]), dsf[c2], dkacc[db]);
           }
-        }
       }
-      if (has_next) {
-        lstore(dos[buf ^ 1]);
-        stats(i + 1, buf ^ 1);
-      }
+    };
+
+    bf16* Q0 = smem;
+    bf16* D0 = smem + TILE;
+    bf16* Q1 = smem + 2 * TILE;
+    bf16* D1 = smem + 3 * TILE;
+    issue(Q0, D0, 0);
+    put_stats(0);
+    wait_vmem();
+    __syncthreads();
+    for (int64_t i = 0; i < n_iter; i += 2) {
+      if (i + 1 < n_iter) issue(Q1, D1, i + 1);
+      tile_step(Q0, D0, stat[0][0], stat[0][1], i);
+      if (i + 1 < n_iter) put_stats(1);
+      wait_vmem();
+      __syncthreads();
+      if (i + 1 >= n_iter) break;
+      if (i + 2 < n_iter) issue(Q0, D0, i + 2);
+      tile_step(Q1, D1, stat[1][0], stat[1][1], i + 1);
+      if (i + 2 < n_iter) put_stats(0);
+      wait_vmem();
       __syncthreads();
     }
   }
