@@ -88,7 +88,7 @@ def run_ring_forward(w, steps, warmup):
     launch_ms = [ev[i][t].elapsed_time(ev[i][t + 1]) for i in range(steps) for t in range(n)]
     assert not torch.isnan(out).any(), "NaN in output"
     return {"wall_s": wall, "launch_ms": launch_ms, "launches_per_step": n, "order": order,
-            "kernel": "fwd_kernel<128>", "src": FWD_SRC}
+            "kernel": f"fwd_kernel<{w.head_dim}>", "src": FWD_SRC}
 
 
 def run_training(w, steps, warmup):
@@ -207,6 +207,83 @@ def copy_calibration(reps):
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": max(reps, 1)}), flush=True)
 
 
+def _result_dbs(d):
+    import glob
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not dbs:
+        sys.exit(f"no rocprofv3 *_results.db under {d}")
+    return dbs
+
+
+def trace_summary(d):
+    """Per-kernel calls, average duration and launch shape from a rocprofv3 --kernel-trace database."""
+    import sqlite3
+    agg = {}
+    for db in _result_dbs(d):
+        con = sqlite3.connect(db)
+        q = ("select name, duration, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, scratch_size, "
+             "lds_size from kernels")
+        for name, dur, gx, wx, vg, ag, sc, lds in con.execute(q):
+            a = agg.setdefault(name, [0, 0.0, gx, wx, vg, ag, sc, lds])
+            a[0] += 1
+            a[1] += dur
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"{a[0]:6d} calls avg {a[1] / a[0] / 1e3:10.3f} us  grid {a[2]} wg {a[3]} vgpr {a[4]} agpr {a[5]} "
+              f"scratch {a[6]} lds {a[7]}  {name[:100]}")
+
+
+def _counter_per_dispatch(d, counter, kernel_substr):
+    """Sum of one counter per dispatch of the kernels whose name contains kernel_substr."""
+    import sqlite3
+    per = {}
+    for db in _result_dbs(d):
+        con = sqlite3.connect(db)
+        q = "select dispatch_id, kernel_name, value from counters_collection where counter_name = ?"
+        for disp, name, val in con.execute(q, (counter,)):
+            if kernel_substr in name:
+                per[(db, disp)] = per.get((db, disp), 0.0) + val
+    return [per[k] for k in sorted(per)]
+
+
+def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
+    """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled
+    by what the same counter reads for a plain copy of 1 GiB; written to the traffic summary that
+    bench.py reports while the kernel source is unchanged."""
+    kern = "fwd_kernel<128>"
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", kern)
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE", kern)
+    cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
+    cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "")
+    n = 1 << 30
+    # the copy launches dominate the calibration runs; take the largest dispatch (the 1 GiB copy)
+    fscale = n / 1024.0 / max(cf)
+    wscale = n / 1024.0 / max(cw)
+    fb = sum(fetch) / len(fetch) * 1024 * fscale
+    wb = sum(write) / len(write) * 1024 * wscale
+    rec = {
+        "kernel": "ba::fwd_kernel<128>",
+        "workload": "llama2_7b_s32k_ring8 (8 ring steps, one dispatch each)",
+        "kernel_source_sha": _src_sha(FWD_SRC),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_copy_fetch -o cfetch -- python -u bench.py --copy-calibration --steps 3",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_copy_write -o cwrite -- python -u bench.py --copy-calibration --steps 3",
+            "python bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
+        ],
+        "copy_calibration": {"bytes_per_copy": n, "fetch_size_kib": max(cf), "write_size_kib": max(cw),
+                             "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
+        "fetch_size_kib_per_dispatch": [round(x, 1) for x in fetch],
+        "write_size_kib_per_dispatch": [round(x, 1) for x in write],
+        "hbm_bytes_per_launch": int(fb + wb),
+        "hbm_fetch_bytes_per_launch": int(fb),
+        "hbm_write_bytes_per_launch": int(wb),
+    }
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"hbm_bytes_per_launch": rec["hbm_bytes_per_launch"], "out": out}))
+
+
 def training_line(w, args):
     """One JSON line for a forward+backward workload (attention training step)."""
     r = run_training(w, args.steps, args.warmup)
@@ -238,7 +315,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print per-kernel statistics of a rocprofv3 --kernel-trace output directory")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_traffic.json"))
+        return
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
@@ -261,7 +348,7 @@ def main():
     achieved = flop / r["launches_per_step"] / (avg_launch_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic("fwd_kernel_d128", r["src"]),
+                "traffic": _traffic("fwd_kernel_d128", r["src"]) if w.head_dim == 128 else None,
                 "kernel": r["kernel"], "avg_launch_ms": round(avg_launch_ms, 4),
                 "launches_per_step": r["launches_per_step"]}
     line = {
