@@ -88,7 +88,63 @@ def run_ring_forward(w, steps, warmup):
     launch_ms = [ev[i][t].elapsed_time(ev[i][t + 1]) for i in range(steps) for t in range(n)]
     assert not torch.isnan(out).any(), "NaN in output"
     return {"wall_s": wall, "launch_ms": launch_ms, "launches_per_step": n, "order": order,
-            "kernel": f"fwd_kernel<{w.head_dim}>", "src": FWD_SRC}
+            "kernel": f"fwd_kernel<{w.head_dim}>", "src": FWD_SRC,
+            "tensors": (q, k, v, o_acc, lse, out)}
+
+
+def _event_ms(fn, reps):
+    """Average milliseconds of fn() over reps calls on the current stream (after one warm call)."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def side_measurements(w, tensors, reps=5):
+    """Measured after the timed region, on the same inputs:
+    - the forward as ONE chunk (S keys in one call), to show what the ring split costs;
+    - the HBM-bound kernels of the path at this shape, as algorithmic bytes / time against 8 TB/s:
+      lse_merge (fp32 O_acc read+written, fp32 partial read, three LSE rows) and the backward's
+      delta preprocess (dO and O read in bf16, delta written); the dQ finalise is fused into the
+      last ring step's dq kernel and has no time of its own."""
+    import torch
+
+    from long_context_exact_blockattn_amd import _lib
+    q, k, v, o_acc, lse, out = tensors
+    b, s, hq, d = q.shape
+    elems, rows = b * s * hq * d, b * s * hq
+
+    def one_shot():
+        _lib.blockattn_fwd(q, k, v, o_acc, lse, mode=_lib.BA_OVERWRITE, o_final=out)
+    ms1 = _event_ms(one_shot, reps)
+    res = {"one_shot": {"ms": round(ms1, 4), "tflops": round(w.fwd_flop() / ms1 / 1e9, 2)}}
+
+    # a finite partial, so that both operands of every row are read (a -inf partial is skipped)
+    o_part = o_acc.clone()
+    lse_part = lse.clone()
+
+    def merge():
+        _lib.lse_merge(o_acc, lse, o_part, lse_part)
+    ms_m = _event_ms(merge, reps)
+    bytes_m = elems * (4 + 4 + 4) + rows * 4 * 3
+    delta = torch.empty_like(lse)
+    k0 = k[:, :0]
+
+    def delta_only():
+        _lib.blockattn_bwd(q, k0, k0, out, out, lse, delta, o_acc, k0, k0, flags=_lib.BA_BWD_COMPUTE_DELTA)
+    ms_d = _event_ms(delta_only, reps)
+    bytes_d = elems * (2 + 2) + rows * 4
+    hbm = {}
+    for name, ms, by in (("lse_merge", ms_m, bytes_m), ("bwd_delta", ms_d, bytes_d)):
+        gbs = by / (ms * 1e-3) / 1e9
+        hbm[name] = {"bytes": by, "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    res["hbm_kernels"] = hbm
+    return res
 
 
 def run_training(w, steps, warmup):
@@ -361,6 +417,9 @@ def main():
                    "chunk_order": r["order"], "causal": True, "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": roofline,
     }
+    side = side_measurements(w, r.pop("tensors"))
+    line["one_shot"] = dict(side["one_shot"], ring_overhead_pct=round(100 * (ms_per_step / side["one_shot"]["ms"] - 1), 2))
+    line["hbm_kernels"] = side["hbm_kernels"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
