@@ -301,6 +301,47 @@ def _counter_per_dispatch(d, counter, kernel_substr):
     return [per[k] for k in sorted(per)]
 
 
+COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS "
+            "SQ_WAIT_ANY SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+
+
+def counter_summary(d):
+    """MFMA-busy beside VALU-busy for the forward kernel, from one rocprofv3 --pmc pass with COUNTERS.
+
+    Per dispatch: cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES (32 per MFMA, summed over SIMDs) / (1024 SIMDs x cycles); VALU busy is
+    estimated from instruction counts at the SIMD issue rates measured on this part (a non-MFMA
+    VALU instruction occupies the SIMD 2 cycles, a transcendental ~6.2); waiting = SQ_WAIT_ANY /
+    SQ_WAVE_CYCLES."""
+    import sqlite3
+    per = {}
+    for db in _result_dbs(d):
+        con = sqlite3.connect(db)
+        q = "select dispatch_id, kernel_name, counter_name, value from counters_collection"
+        for disp, name, cname, val in con.execute(q):
+            if "fwd_kernel<128>" in name:
+                rec = per.setdefault((db, disp), {})
+                rec[cname] = rec.get(cname, 0.0) + val
+    rows = []
+    for key in sorted(per):
+        c = per[key]
+        cyc = c["GRBM_GUI_ACTIVE"] / 8.0
+        valu = c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]
+        rows.append({
+            "mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc),
+            "valu_busy_est": (2.0 * valu + 4.2 * c["SQ_INSTS_VALU_TRANS_F32"]) / (1024 * cyc),
+            "valu_per_mfma": valu / c["SQ_INSTS_MFMA"],
+            "trans_per_mfma": c["SQ_INSTS_VALU_TRANS_F32"] / c["SQ_INSTS_MFMA"],
+            "lds_per_mfma": c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"],
+            "wave_waiting": c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"],
+            "mfma": c["SQ_INSTS_MFMA"],
+        })
+    tot = sum(r["mfma"] for r in rows)
+    print(f"{len(rows)} dispatches of fwd_kernel<128>; MFMA-weighted averages:")
+    for k in ("mfma_busy", "valu_busy_est", "valu_per_mfma", "trans_per_mfma", "lds_per_mfma", "wave_waiting"):
+        print(f"  {k:15s} {sum(r[k] * r['mfma'] for r in rows) / tot:8.3f}")
+
+
 def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
     """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled
     by what the same counter reads for a plain copy of 1 GiB; written to the traffic summary that
@@ -321,8 +362,8 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
         "workload": "llama2_7b_s32k_ring8 (8 ring steps, one dispatch each)",
         "kernel_source_sha": _src_sha(FWD_SRC),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_copy_fetch -o cfetch -- python -u bench.py --copy-calibration --steps 3",
             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_copy_write -o cwrite -- python -u bench.py --copy-calibration --steps 3",
             "python bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
@@ -371,11 +412,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
+    ap.add_argument("--no-side-measurements", action="store_true",
+                    help="skip the one-chunk forward and the HBM-bound kernel timings (for profiled runs)")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="print MFMA-busy and VALU-busy of the forward kernel from a rocprofv3 --pmc run "
+                         "with the counters in bench.COUNTERS")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel statistics of a rocprofv3 --kernel-trace output directory")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary)
         return
@@ -417,9 +466,12 @@ def main():
                    "chunk_order": r["order"], "causal": True, "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": roofline,
     }
-    side = side_measurements(w, r.pop("tensors"))
-    line["one_shot"] = dict(side["one_shot"], ring_overhead_pct=round(100 * (ms_per_step / side["one_shot"]["ms"] - 1), 2))
-    line["hbm_kernels"] = side["hbm_kernels"]
+    tensors = r.pop("tensors")
+    if not args.no_side_measurements:
+        side = side_measurements(w, tensors)
+        line["one_shot"] = dict(side["one_shot"],
+                                ring_overhead_pct=round(100 * (ms_per_step / side["one_shot"]["ms"] - 1), 2))
+        line["hbm_kernels"] = side["hbm_kernels"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
