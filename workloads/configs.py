@@ -1,4 +1,4 @@
-"""The five workload shapes used for parity tests and throughput measurement.
+"""The workload shapes used for parity tests and throughput measurement.
 
 Each entry names what it is: the model whose attention shape it copies, the
 sequence length, and how the key/value sequence is streamed (ring steps of
@@ -60,6 +60,11 @@ CONFIGS = {
     "gqa_llama3_8b_s128k_ring16": Workload(
         "gqa_llama3_8b_s128k_ring16", 1, 32, 8, 131072, 128, n_chunks=16,
         description="Llama-3-8B GQA (32 q heads, 8 kv heads), S=131072, 16 ring chunks of 8192, forward"),
+    "s2attn_llama2_7b_s100k_g25600": Workload(
+        "s2attn_llama2_7b_s100k_g25600", 1, 32, 32, 102400, 128, s2_group=25600, s2_shift_head0=16,
+        backward=True,
+        description="S2-Attn at long context: Llama-2-7B shape, S=102400, group S/4=25600, heads 16-31 "
+                    "shifted by 12800, forward + backward"),
     "llama2_13b_s64k_ring8_train": Workload(
         "llama2_13b_s64k_ring8_train", 1, 40, 40, 65536, 128, n_chunks=8, backward=True,
         description="Llama-2-13B attention shape, S=65536, 8 ring chunks of 8192, forward + backward"),
@@ -72,6 +77,7 @@ ALIASES = {
     "c3": "s2attn_llama2_7b_s8k_g2048",
     "c4": "gqa_llama3_8b_s128k_ring16",
     "c5": "llama2_13b_s64k_ring8_train",
+    "s2_100k": "s2attn_llama2_7b_s100k_g25600",
 }
 
 
