@@ -144,6 +144,28 @@ def side_measurements(w, tensors, reps=5):
         gbs = by / (ms * 1e-3) / 1e9
         hbm[name] = {"bytes": by, "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
     res["hbm_kernels"] = hbm
+
+    # the ring's receive side: each step's chunk copied into one of two staging buffers on a
+    # second stream while the previous step computes, against the plain ring on resident chunks
+    if w.n_chunks > 1:
+        import long_context_exact_blockattn_amd as ba
+        from workloads import chunk_order
+        order = chunk_order(w.n_chunks, seed=w.seed)
+        ms_plain = _event_ms(lambda: ba.ring_forward(q, k, v, w.n_chunks, order, o_acc=o_acc, lse=lse, out=out),
+                             reps)
+        ms_staged = _event_ms(lambda: ba.ring_forward_staged(q, k, v, w.n_chunks, order), reps)
+        kb = torch.empty_like(k)
+        vb = torch.empty_like(v)
+
+        def copies():
+            kb.copy_(k)
+            vb.copy_(v)
+        ms_copy = _event_ms(copies, reps)
+        chunk_bytes = 2 * k.numel() * k.element_size() // w.n_chunks
+        res["ring_staged"] = {"plain_ms": round(ms_plain, 4), "staged_ms": round(ms_staged, 4),
+                              "overhead_pct": round(100 * (ms_staged / ms_plain - 1), 2),
+                              "copy_bytes_per_step": chunk_bytes,
+                              "copy_alone_ms_per_step": round(ms_copy / w.n_chunks, 4)}
     return res
 
 
@@ -472,6 +494,8 @@ def main():
         line["one_shot"] = dict(side["one_shot"],
                                 ring_overhead_pct=round(100 * (ms_per_step / side["one_shot"]["ms"] - 1), 2))
         line["hbm_kernels"] = side["hbm_kernels"]
+        if "ring_staged" in side:
+            line["ring_staged"] = side["ring_staged"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

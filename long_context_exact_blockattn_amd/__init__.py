@@ -8,11 +8,11 @@ from . import _lib
 from ._lib import (BA_ACCUMULATE, BA_BWD_COMPUTE_DELTA, BA_BWD_FINALIZE_DQ, BA_OVERWRITE,
                    BlockAttnError, blockattn_bwd, blockattn_fwd, lse_merge, s2attn_bwd, s2attn_fwd,
                    status_string)
-from .ring import ring_backward, ring_forward
+from .ring import ring_backward, ring_forward, ring_forward_staged
 from .s2 import s2_backward, s2_forward
 
 __all__ = [
     "BA_ACCUMULATE", "BA_BWD_COMPUTE_DELTA", "BA_BWD_FINALIZE_DQ", "BA_OVERWRITE", "BlockAttnError",
     "blockattn_bwd", "blockattn_fwd", "lse_merge", "s2attn_bwd", "s2attn_fwd", "status_string",
-    "ring_backward", "ring_forward", "s2_backward", "s2_forward",
+    "ring_backward", "ring_forward", "ring_forward_staged", "s2_backward", "s2_forward",
 ]

@@ -112,8 +112,9 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """A hipStream_t from None (torch's current stream), a torch stream, or a raw handle."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 

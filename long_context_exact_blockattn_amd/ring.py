@@ -46,6 +46,62 @@ def ring_forward(q, k, v, n_chunks, order=None, *, causal=True, scale=None, o_ac
     return out, lse, o_acc
 
 
+def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=None, copy_stream=None):
+    """ring_forward with every step's key/value chunk first copied into one of two staging buffers
+    on a second stream, the copy for step t+1 running while step t computes.
+
+    This is the receive side of a ring on one device: on a ring of hosts the next block arrives
+    over the interconnect while the current one is being used (Ring Attention summary, Summary),
+    and the method has no overhead when the compute of a step outlasts the transfer of a block.
+    Here the transfer is a device-to-device copy of the same bytes.  The compute of step t waits
+    for the copy of its chunk (event); the copy into a staging buffer waits for the compute that
+    last read it (event), so the two buffers alternate.  Both streams have the default priority.
+    Returns (out bf16, lse fp32, o_acc fp32), equal bit for bit to ring_forward's.
+    """
+    bounds = _bounds(k.shape[1], n_chunks)
+    order = list(range(len(bounds))) if order is None else list(order)
+    if sorted(order) != list(range(len(bounds))):
+        raise ValueError("order must be a permutation of the chunk indices")
+    b, s, hq, d = q.shape
+    main = torch.cuda.current_stream(q.device)
+    side = torch.cuda.Stream(device=q.device) if copy_stream is None else copy_stream
+    cmax = max(c1 - c0 for c0, c1 in bounds)
+    kbuf = [torch.empty(b, cmax, k.shape[2], d, device=k.device, dtype=k.dtype) for _ in range(2)]
+    vbuf = [torch.empty(b, cmax, v.shape[2], d, device=v.device, dtype=v.dtype) for _ in range(2)]
+    o_acc = torch.empty(b, s, hq, d, device=q.device, dtype=torch.float32)
+    lse = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
+    out = torch.empty(b, s, hq, d, device=q.device, dtype=torch.bfloat16)
+    copied = [torch.cuda.Event() for _ in range(2)]
+    computed = [torch.cuda.Event() for _ in range(2)]
+    side.wait_stream(main)  # the inputs and the buffers exist before any copy reads or fills them
+
+    def copy(t):
+        slot = t % 2
+        c0, c1 = bounds[order[t]]
+        with torch.cuda.stream(side):
+            if t >= 2:
+                side.wait_event(computed[slot])
+            kbuf[slot][:, : c1 - c0].copy_(k[:, c0:c1], non_blocking=True)
+            vbuf[slot][:, : c1 - c0].copy_(v[:, c0:c1], non_blocking=True)
+            copied[slot].record(side)
+
+    copy(0)
+    for t in range(len(order)):
+        slot = t % 2
+        c0, c1 = bounds[order[t]]
+        if t + 1 < len(order):
+            copy(t + 1)
+        main.wait_event(copied[slot])
+        _lib.blockattn_fwd(q, kbuf[slot][:, : c1 - c0], vbuf[slot][:, : c1 - c0], o_acc, lse,
+                           mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
+                           o_final=out if t == len(order) - 1 else None,
+                           k_pos0=c0, causal=causal, scale=scale, stream=main)
+        computed[slot].record(main)
+    for t in kbuf + vbuf:
+        t.record_stream(side)
+    return out, lse, o_acc
+
+
 def ring_backward(q, k, v, o, dout, lse, n_chunks, order=None, *, causal=True, scale=None,
                   dkv_dtype=torch.bfloat16, stream=None):
     """Backward over key/value chunks: returns (dq bf16, dk, dv).

@@ -237,3 +237,20 @@ def test_full_size_ring_sampled(name):
     log(f"{name} order={order} heads={heads} rows={len(rows)}: O {worst_o:.3e} LSE {worst_l:.3e}")
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
     assert not torch.isnan(o_acc).any()
+
+
+@pytest.mark.parametrize("n_chunks,S,B", [(8, 2048, 1), (3, 1000, 2)])
+def test_ring_forward_staged_equals_ring_forward(n_chunks, S, B):
+    """Chunks received into double buffers on a second stream give the same bits as the plain ring."""
+    H, D = 4, 128
+    q, k, v = make_inputs(B, S, H, H, D, seed=60 + n_chunks)
+    qd, kd, vd = q.to(dev()), k.to(dev()), v.to(dev())
+    order = chunk_order(n_chunks, seed=1)
+    ref = ba.ring_forward(qd, kd, vd, n_chunks, order)
+    got = ba.ring_forward_staged(qd, kd, vd, n_chunks, order)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
+    o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v))
+    log(f"staged ring n={n_chunks} S={S} B={B}: max |O - O_ref| {max_err(got[0], o_ref):.3e}")
+    assert max_err(got[2], o_ref) <= TOL_O and max_err(got[1], lse_ref) <= TOL_LSE
