@@ -139,8 +139,17 @@ def side_measurements(w, tensors, reps=5):
         _lib.blockattn_bwd(q, k0, k0, out, out, lse, delta, o_acc, k0, k0, flags=_lib.BA_BWD_COMPUTE_DELTA)
     ms_d = _event_ms(delta_only, reps)
     bytes_d = elems * (2 + 2) + rows * 4
+    # Ulysses layout permutes at one device's share of this workload on 8 devices (S/8 rows, all
+    # heads): every element read once and written once
+    n_dev = 8
+    x_share = q[:, : s // n_dev].contiguous()
+    send = _lib.ulysses_pack(x_share, n_dev)
+    ms_pack = _event_ms(lambda: _lib.ulysses_pack(x_share, n_dev, send=send), reps * 4)
+    ms_unpack = _event_ms(lambda: _lib.ulysses_unpack(send, n_dev, x=x_share), reps * 4)
+    bytes_u = 2 * x_share.numel() * x_share.element_size()
     hbm = {}
-    for name, ms, by in (("lse_merge", ms_m, bytes_m), ("bwd_delta", ms_d, bytes_d)):
+    for name, ms, by in (("lse_merge", ms_m, bytes_m), ("bwd_delta", ms_d, bytes_d),
+                         ("ulysses_pack", ms_pack, bytes_u), ("ulysses_unpack", ms_unpack, bytes_u)):
         gbs = by / (ms * 1e-3) / 1e9
         hbm[name] = {"bytes": by, "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
     res["hbm_kernels"] = hbm

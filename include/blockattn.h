@@ -165,6 +165,32 @@ int s2attn_bwd(const ba_desc* desc, const ba_s2_desc* s2, const void* q, const v
                float* delta, float* dq_acc, void* dk, void* dv, int32_t dkv_dtype,
                void* dq_final, int32_t flags, hipStream_t stream);
 
+/* ---- Ulysses sequence parallelism: the layout permutes around its all-to-all ----
+ * DeepSpeed Ulysses, one of the sequence-parallel methods the long-context
+ * recipe supports beside Ring Attention (project page "How It Works"; the Ring
+ * Attention summary's references), shards the sequence over N devices and
+ * exchanges it for a head sharding around attention.  Device r holds
+ * x = [B, Sl, H, D] (its Sl =
+ * S / N rows, all heads).  These two calls are the device's local halves of the
+ * exchange (the all-to-all itself needs N devices and is not here):
+ *   ulysses_pack:    send[n][b][s][j][d] = x[b][s][n*(H/N) + j][d]
+ *                    (send block n, [B, Sl, H/N, D], goes to device n)
+ *   ulysses_unpack:  x[b][s][n*(H/N) + j][d] = recv[n][b][s][j][d]
+ *                    (recv block n came from device n)
+ * For B = 1, the blocks a device receives after packing, in source order, are
+ * already the dense [1, S, H/N, D] tensor of its heads over the whole
+ * sequence, which the attention calls take as is; the output goes back through
+ * the same exchange and ulysses_unpack.
+ * All tensors are dense (row-major in the index order shown), bf16, 16-byte
+ * aligned; head_dim a multiple of 8; heads % n_devices == 0; src and dst must
+ * not overlap.  Bit-exact copies.  Errors: BA_ERR_NULL, BA_ERR_SHAPE (negative
+ * size, n_devices < 1, heads % n_devices != 0, head_dim % 8 != 0), BA_ERR_ALIGN,
+ * BA_ERR_LAUNCH.  Zero-size problems return BA_OK without launching. */
+int ulysses_pack(const void* x, void* send, int64_t batch, int64_t seqlen_local, int32_t heads,
+                 int32_t head_dim, int32_t n_devices, hipStream_t stream);
+int ulysses_unpack(const void* recv, void* x, int64_t batch, int64_t seqlen_local, int32_t heads,
+                   int32_t head_dim, int32_t n_devices, hipStream_t stream);
+
 /* Human-readable name of a ba_status value (static storage). */
 const char* blockattn_status_string(int status);
 

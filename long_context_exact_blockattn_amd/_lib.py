@@ -79,6 +79,10 @@ def load():
     lib.s2attn_fwd.restype = ctypes.c_int
     lib.s2attn_bwd.argtypes = [D, S2, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
     lib.s2attn_bwd.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    for fn in (lib.ulysses_pack, lib.ulysses_unpack):
+        fn.argtypes = [P, P, i64, i64, i32, i32, i32, P]
+        fn.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_debug_fwd_schedule.argtypes = [D, S2, i32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
@@ -238,6 +242,46 @@ def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_hea
                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
                            _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
     _check(st, "s2attn_bwd")
+
+
+def _dense_bf16(t, name, fn):
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise BlockAttnError(BA_ERR_UNSUPPORTED, f"{fn} ({name} must be bf16)")
+    if not t.is_contiguous():
+        raise BlockAttnError(BA_ERR_STRIDE, f"{fn} ({name} must be dense)")
+
+
+def ulysses_pack(x, n_devices, *, send=None, stream=None):
+    """x [B, Sl, H, D] -> send [N, B, Sl, H/N, D]; see ulysses_pack in include/blockattn.h."""
+    import torch
+    _dense_bf16(x, "x", "ulysses_pack")
+    b, sl, h, d = x.shape
+    if send is None:
+        send = torch.empty((n_devices, b, sl, h // max(n_devices, 1), d), device=x.device, dtype=x.dtype)
+    _dense_bf16(send, "send", "ulysses_pack")
+    if send.numel() != x.numel():
+        raise BlockAttnError(BA_ERR_SHAPE, "ulysses_pack (send must hold as many elements as x)")
+    st = load().ulysses_pack(_ptr(x), _ptr(send), b, sl, h, d, n_devices, _stream(stream))
+    _check(st, "ulysses_pack")
+    return send
+
+
+def ulysses_unpack(recv, n_devices, *, x=None, stream=None):
+    """recv [N, B, Sl, H/N, D] -> x [B, Sl, H, D]; see ulysses_unpack in include/blockattn.h."""
+    import torch
+    _dense_bf16(recv, "recv", "ulysses_unpack")
+    n, b, sl, hn, d = recv.shape
+    if n != n_devices:
+        raise BlockAttnError(BA_ERR_SHAPE, "ulysses_unpack (recv's first axis must be n_devices)")
+    if x is None:
+        x = torch.empty((b, sl, hn * n, d), device=recv.device, dtype=recv.dtype)
+    _dense_bf16(x, "x", "ulysses_unpack")
+    if x.numel() != recv.numel():
+        raise BlockAttnError(BA_ERR_SHAPE, "ulysses_unpack (x must hold as many elements as recv)")
+    st = load().ulysses_unpack(_ptr(recv), _ptr(x), b, sl, hn * n, d, n_devices, _stream(stream))
+    _check(st, "ulysses_unpack")
+    return x
 
 
 def debug_fwd_schedule(desc, head, s2=None):

@@ -9,6 +9,7 @@
 #include "ba_fwd.h"
 #include "ba_merge.h"
 #include "ba_schedule.h"
+#include "ba_ulysses.h"
 
 namespace {
 
@@ -174,6 +175,31 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   return BA_OK;
 }
 
+int ulysses_launch(bool pack, const void* src, void* dst, int64_t batch, int64_t seqlen_local,
+                     int32_t heads, int32_t head_dim, int32_t n_devices, hipStream_t stream) {
+  if (batch < 0 || seqlen_local < 0 || heads < 0 || head_dim < 0 || n_devices < 1) return BA_ERR_SHAPE;
+  if (heads % n_devices != 0 || head_dim % 8 != 0) return BA_ERR_SHAPE;
+  const int64_t n_chunks = batch * seqlen_local * heads * (head_dim / 8);
+  if (n_chunks == 0) return BA_OK;
+  if (!src || !dst) return BA_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return BA_ERR_ALIGN;
+  UlyssesArgs a;
+  a.src = (const u32x4*)src;
+  a.dst = (u32x4*)dst;
+  a.B = batch;
+  a.Sl = seqlen_local;
+  a.H = heads;
+  a.CPD = head_dim / 8;
+  a.N = n_devices;
+  a.n_chunks = n_chunks;
+  const int64_t blocks = (n_chunks + 255) / 256;
+  if (pack)
+    hipLaunchKernelGGL(ulysses_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(ulysses_unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -227,6 +253,16 @@ int s2attn_bwd(const ba_desc* desc, const ba_s2_desc* s2, const void* q, const v
   if (!desc || !s2) return BA_ERR_NULL;
   return bwd_impl(desc, s2, q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dkv_dtype, dq_final,
                   flags, stream);
+}
+
+int ulysses_pack(const void* x, void* send, int64_t batch, int64_t seqlen_local, int32_t heads,
+                 int32_t head_dim, int32_t n_devices, hipStream_t stream) {
+  return ulysses_launch(true, x, send, batch, seqlen_local, heads, head_dim, n_devices, stream);
+}
+
+int ulysses_unpack(const void* recv, void* x, int64_t batch, int64_t seqlen_local, int32_t heads,
+                   int32_t head_dim, int32_t n_devices, hipStream_t stream) {
+  return ulysses_launch(false, recv, x, batch, seqlen_local, heads, head_dim, n_devices, stream);
 }
 
 const char* blockattn_status_string(int status) {

@@ -38,3 +38,4 @@ __all__ = [
     "ring_attention_forward",
     "rows_forward",
 ]
+from . import ulysses  # noqa: E402,F401  (layout permutes of Ulysses sequence parallelism)

@@ -164,3 +164,15 @@ def test_schedule_longest_first(lib):
         tiles[-1][1] += 1
     work = [t[1] for t in tiles]
     assert work == sorted(work, reverse=True)
+
+
+def test_ulysses_validation(lib):
+    P = ctypes.c_void_p
+    for fn in (lib.ulysses_pack, lib.ulysses_unpack):
+        assert fn(P(FAKE), P(FAKE), 1, 16, 30, 128, 8, None) == _lib.BA_ERR_SHAPE    # heads % N
+        assert fn(P(FAKE), P(FAKE), 1, 16, 32, 128, 0, None) == _lib.BA_ERR_SHAPE    # N < 1
+        assert fn(P(FAKE), P(FAKE), 1, 16, 32, 100, 8, None) == _lib.BA_ERR_SHAPE    # D % 8
+        assert fn(P(FAKE), P(FAKE), -1, 16, 32, 128, 8, None) == _lib.BA_ERR_SHAPE
+        assert fn(None, P(FAKE), 1, 16, 32, 128, 8, None) == _lib.BA_ERR_NULL
+        assert fn(P(FAKE), P(FAKE + 8), 1, 16, 32, 128, 8, None) == _lib.BA_ERR_ALIGN
+        assert fn(None, None, 1, 0, 32, 128, 8, None) == _lib.BA_OK                  # zero size, no launch
