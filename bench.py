@@ -412,6 +412,76 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
     print(json.dumps({"hbm_bytes_per_launch": rec["hbm_bytes_per_launch"], "out": out}))
 
 
+def ffn_cpu_baseline(w, sample_rows=32768):
+    """The feedforward oracle as it stands, on the first sample_rows rows with the full weights."""
+    import numpy as np
+
+    from oracle.ffn import swiglu_ffn
+    from workloads import make_ffn_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    x, w1, w3, w2 = make_ffn_inputs(w.rows, w.d_model, w.d_ff, seed=w.seed)
+    sample_rows = min(sample_rows, w.rows)
+    xs = x[:sample_rows].float().numpy().astype(np.float64)
+    w1n, w3n, w2n = (t.float().numpy().astype(np.float64) for t in (w1, w3, w2))
+    t0 = time.perf_counter()
+    swiglu_ffn(xs, w1n, w3n, w2n)
+    dt = time.perf_counter() - t0
+    flop = 6.0 * sample_rows * w.d_model * w.d_ff
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: the first {sample_rows} of {w.rows} rows with the full weights, numpy "
+                      f"float64; {dt:.2f} s for {flop:.3e} algorithmic flop"}
+
+
+def ffn_line(w, args):
+    """One JSON line for the blockwise feedforward workload (two GEMM launches per row block)."""
+    import torch
+
+    import long_context_exact_blockattn_amd as ba
+    from workloads import make_ffn_inputs
+    dev = torch.device("cuda:0")
+    x, w1, w3, w2 = (t.to(dev) for t in make_ffn_inputs(w.rows, w.d_model, w.d_ff, seed=w.seed))
+    out = torch.empty_like(x)
+    hidden = torch.empty(w.block_rows, w.d_ff, device=dev, dtype=torch.bfloat16)
+
+    def step():
+        ba.bpt_ffn(x, w1, w3, w2, block_rows=w.block_rows, out=out, hidden=hidden)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    tflops = w.flop() / (ms * 1e-3) / 1e12
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    achieved = w.flop() / (ev_ms * 1e-3) / 1e12
+    launches = 2 * -(-w.rows // w.block_rows)
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {"workload": w.name, "rows": w.rows, "d_model": w.d_model, "d_ff": w.d_ff,
+                   "block_rows": w.block_rows, "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_nt_kernel (SwiGLU and plain epilogues)",
+                     "avg_launch_ms": round(ev_ms / launches, 4), "launches_per_step": launches},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = ffn_cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
 def training_line(w, args):
     """One JSON line for a forward+backward workload (attention training step)."""
     r = run_training(w, args.steps, args.warmup)
@@ -470,7 +540,10 @@ def main():
               "devices) is not part of this build; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    from workloads import get
+    from workloads import FFN_CONFIGS, get
+    if args.workload in FFN_CONFIGS:
+        ffn_line(FFN_CONFIGS[args.workload], args)
+        return
     w = get(args.workload)
     if w.s2_group is not None or w.backward:
         training_line(w, args)

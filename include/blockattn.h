@@ -191,6 +191,24 @@ int ulysses_pack(const void* x, void* send, int64_t batch, int64_t seqlen_local,
 int ulysses_unpack(const void* recv, void* x, int64_t batch, int64_t seqlen_local, int32_t heads,
                    int32_t head_dim, int32_t n_devices, hipStream_t stream);
 
+/* ---- Blockwise feedforward (BPT) ----
+ * Each host of the ring computes attention and the feedforward for its query
+ * block, block by block (Ring Attention summary, Summary; the blockwise
+ * parallel transformer runs the feedforward per block so the hidden activation
+ * of the whole sequence never exists, Key points).  The feedforward of the
+ * models the pages train (LLaMA / Llama-2) is SwiGLU:
+ *   out = (silu(x W1^T) * (x W3^T)) W2^T,  silu(z) = z / (1 + exp(-z)).
+ * x, out: [rows, d_model]; w1, w3: [d_ff, d_model]; w2: [d_model, d_ff]
+ * (row-major, the [out, in] layout of a linear layer); hidden: caller-owned
+ * workspace of at least min(block_rows, rows) x d_ff elements.  All bf16, dense,
+ * 16-byte aligned.  Rows are processed in blocks of block_rows, each as two
+ * launches (hidden = silu(x W1^T) * (x W3^T) rounded to bf16, then
+ * out = hidden W2^T), fp32 accumulation, bf16 stores (round to nearest even).
+ * Requirements: d_model % 256 == 0, d_ff % 128 == 0, every operand under 2^31
+ * elements.  Errors: BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_ALIGN, BA_ERR_LAUNCH. */
+int bpt_ffn(const void* x, const void* w1, const void* w3, const void* w2, void* out, void* hidden,
+            int64_t rows, int32_t d_model, int32_t d_ff, int64_t block_rows, hipStream_t stream);
+
 /* Human-readable name of a ba_status value (static storage). */
 const char* blockattn_status_string(int status);
 

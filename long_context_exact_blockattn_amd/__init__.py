@@ -7,7 +7,7 @@ sequential ring-step and S2 drivers, which only issue library calls.
 from . import _lib
 from ._lib import (BA_ACCUMULATE, BA_BWD_COMPUTE_DELTA, BA_BWD_FINALIZE_DQ, BA_OVERWRITE,
                    BlockAttnError, blockattn_bwd, blockattn_fwd, lse_merge, s2attn_bwd, s2attn_fwd,
-                   status_string, ulysses_pack, ulysses_unpack)
+                   bpt_ffn, status_string, ulysses_pack, ulysses_unpack)
 from .ring import ring_backward, ring_forward, ring_forward_staged
 from .s2 import s2_backward, s2_forward
 
@@ -15,5 +15,5 @@ __all__ = [
     "BA_ACCUMULATE", "BA_BWD_COMPUTE_DELTA", "BA_BWD_FINALIZE_DQ", "BA_OVERWRITE", "BlockAttnError",
     "blockattn_bwd", "blockattn_fwd", "lse_merge", "s2attn_bwd", "s2attn_fwd", "status_string",
     "ring_backward", "ring_forward", "ring_forward_staged", "s2_backward", "s2_forward",
-    "ulysses_pack", "ulysses_unpack",
+    "ulysses_pack", "ulysses_unpack", "bpt_ffn",
 ]

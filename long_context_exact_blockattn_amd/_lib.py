@@ -83,6 +83,8 @@ def load():
     for fn in (lib.ulysses_pack, lib.ulysses_unpack):
         fn.argtypes = [P, P, i64, i64, i32, i32, i32, P]
         fn.restype = ctypes.c_int
+    lib.bpt_ffn.argtypes = [P, P, P, P, P, P, i64, i32, i32, i64, P]
+    lib.bpt_ffn.restype = ctypes.c_int
     lib.blockattn_status_string.argtypes = [ctypes.c_int]
     lib.blockattn_status_string.restype = ctypes.c_char_p
     lib.blockattn_debug_fwd_schedule.argtypes = [D, S2, i32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64]
@@ -282,6 +284,30 @@ def ulysses_unpack(recv, n_devices, *, x=None, stream=None):
     st = load().ulysses_unpack(_ptr(recv), _ptr(x), b, sl, hn * n, d, n_devices, _stream(stream))
     _check(st, "ulysses_unpack")
     return x
+
+
+def bpt_ffn(x, w1, w3, w2, *, block_rows=4096, out=None, hidden=None, stream=None):
+    """SwiGLU feedforward of the rows of x [rows, d_model], block by block; see bpt_ffn in
+    include/blockattn.h.  hidden is the [block_rows, d_ff] workspace (allocated if None)."""
+    import torch
+    for name, t in (("x", x), ("w1", w1), ("w3", w3), ("w2", w2)):
+        _dense_bf16(t, name, "bpt_ffn")
+    rows, d_model = x.shape
+    d_ff = w1.shape[0]
+    if w1.shape != (d_ff, d_model) or w3.shape != (d_ff, d_model) or w2.shape != (d_model, d_ff):
+        raise BlockAttnError(BA_ERR_SHAPE, "bpt_ffn (w1, w3 must be [d_ff, d_model], w2 [d_model, d_ff])")
+    if out is None:
+        out = torch.empty_like(x)
+    if hidden is None:
+        hidden = torch.empty((min(block_rows, max(rows, 1)), d_ff), device=x.device, dtype=x.dtype)
+    _dense_bf16(out, "out", "bpt_ffn")
+    _dense_bf16(hidden, "hidden", "bpt_ffn")
+    if out.shape != x.shape or hidden.numel() < min(block_rows, rows) * d_ff:
+        raise BlockAttnError(BA_ERR_SHAPE, "bpt_ffn (out must match x; hidden must hold block_rows x d_ff)")
+    st = load().bpt_ffn(_ptr(x), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out), _ptr(hidden), rows, d_model, d_ff,
+                        block_rows, _stream(stream))
+    _check(st, "bpt_ffn")
+    return out
 
 
 def debug_fwd_schedule(desc, head, s2=None):

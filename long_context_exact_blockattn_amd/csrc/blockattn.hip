@@ -4,8 +4,11 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "ba_bwd.h"
 #include "ba_common.h"
+#include "ba_ffn.h"
 #include "ba_fwd.h"
 #include "ba_merge.h"
 #include "ba_schedule.h"
@@ -200,6 +203,26 @@ int ulysses_launch(bool pack, const void* src, void* dst, int64_t batch, int64_t
   return launched();
 }
 
+int gemm_launch(int epi, const void* a, const void* b, const void* b3, void* c, int64_t m, int32_t k,
+                int32_t n_out, hipStream_t stream) {
+  GemmArgs g;
+  g.a = (const bf16*)a;
+  g.b = (const bf16*)b;
+  g.b3 = (const bf16*)b3;
+  g.c = (bf16*)c;
+  g.M = m;
+  g.K = k;
+  g.n_out = n_out;
+  g.tiles_m = (int32_t)((m + kGemmBM - 1) / kGemmBM);
+  g.tiles_n = n_out / (epi == EPI_SWIGLU ? 128 : 256);
+  g.n_items = (int64_t)g.tiles_m * g.tiles_n;
+  if (epi == EPI_SWIGLU)
+    hipLaunchKernelGGL(gemm_nt_kernel<EPI_SWIGLU>, dim3((unsigned)g.n_items), dim3(kGemmThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<EPI_STORE>, dim3((unsigned)g.n_items), dim3(kGemmThreads), 0, stream, g);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +286,30 @@ int ulysses_pack(const void* x, void* send, int64_t batch, int64_t seqlen_local,
 int ulysses_unpack(const void* recv, void* x, int64_t batch, int64_t seqlen_local, int32_t heads,
                    int32_t head_dim, int32_t n_devices, hipStream_t stream) {
   return ulysses_launch(false, recv, x, batch, seqlen_local, heads, head_dim, n_devices, stream);
+}
+
+int bpt_ffn(const void* x, const void* w1, const void* w3, const void* w2, void* out, void* hidden,
+            int64_t rows, int32_t d_model, int32_t d_ff, int64_t block_rows, hipStream_t stream) {
+  if (rows < 0 || d_model < 0 || d_ff < 0 || block_rows < 1) return BA_ERR_SHAPE;
+  if (d_model % 256 != 0 || d_ff % 128 != 0) return BA_ERR_SHAPE;
+  if (rows == 0 || d_model == 0 || d_ff == 0) return BA_OK;
+  if (!x || !w1 || !w3 || !w2 || !out || !hidden) return BA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(hidden, 16))
+    return BA_ERR_ALIGN;
+  // the kernels address operands with 32-bit element offsets
+  const int64_t bm = std::min(block_rows, rows);
+  const int64_t lim = (int64_t)1 << 31;
+  if (rows * (int64_t)d_model >= lim || bm * (int64_t)d_ff >= lim || (int64_t)d_ff * d_model >= lim)
+    return BA_ERR_SHAPE;
+  for (int64_t r0 = 0; r0 < rows; r0 += block_rows) {
+    const int64_t m = std::min(block_rows, rows - r0);
+    int r = gemm_launch(EPI_SWIGLU, (const bf16*)x + r0 * d_model, w1, w3, hidden, m, d_model, d_ff, stream);
+    if (r) return r;
+    r = gemm_launch(EPI_STORE, hidden, w2, nullptr, (bf16*)out + r0 * d_model, m, d_ff, d_model, stream);
+    if (r) return r;
+  }
+  return BA_OK;
 }
 
 const char* blockattn_status_string(int status) {

@@ -39,3 +39,4 @@ __all__ = [
     "rows_forward",
 ]
 from . import ulysses  # noqa: E402,F401  (layout permutes of Ulysses sequence parallelism)
+from . import ffn  # noqa: E402,F401  (blockwise feedforward, SwiGLU)

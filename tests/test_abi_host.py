@@ -176,3 +176,15 @@ def test_ulysses_validation(lib):
         assert fn(None, P(FAKE), 1, 16, 32, 128, 8, None) == _lib.BA_ERR_NULL
         assert fn(P(FAKE), P(FAKE + 8), 1, 16, 32, 128, 8, None) == _lib.BA_ERR_ALIGN
         assert fn(None, None, 1, 0, 32, 128, 8, None) == _lib.BA_OK                  # zero size, no launch
+
+
+def test_bpt_ffn_validation(lib):
+    P = ctypes.c_void_p
+    args = [P(FAKE)] * 6
+    assert lib.bpt_ffn(*args, 100, 300, 256, 64, None) == _lib.BA_ERR_SHAPE     # d_model % 256
+    assert lib.bpt_ffn(*args, 100, 256, 200, 64, None) == _lib.BA_ERR_SHAPE     # d_ff % 128
+    assert lib.bpt_ffn(*args, 100, 256, 256, 0, None) == _lib.BA_ERR_SHAPE      # block_rows
+    assert lib.bpt_ffn(*args, 1 << 24, 256, 256, 64, None) == _lib.BA_ERR_SHAPE  # 2^32 elements of x
+    assert lib.bpt_ffn(None, *args[1:], 100, 256, 256, 64, None) == _lib.BA_ERR_NULL
+    assert lib.bpt_ffn(P(FAKE + 2), *args[1:], 100, 256, 256, 64, None) == _lib.BA_ERR_ALIGN
+    assert lib.bpt_ffn(None, None, None, None, None, None, 0, 256, 256, 64, None) == _lib.BA_OK

@@ -9,7 +9,8 @@ Workload shapes follow the attention shapes of the models the pages name
 values standing in for activations (the pages train on PG19 / RedPajama /
 ShareGPT text with trained weights; none of that is used here).
 """
-from .configs import CONFIGS, Workload, get
-from .generate import chunk_order, make_inputs, chunk_bounds
+from .configs import CONFIGS, FFN_CONFIGS, FfnWorkload, Workload, get
+from .generate import chunk_bounds, chunk_order, make_ffn_inputs, make_inputs
 
-__all__ = ["CONFIGS", "Workload", "get", "chunk_order", "make_inputs", "chunk_bounds"]
+__all__ = ["CONFIGS", "FFN_CONFIGS", "FfnWorkload", "Workload", "get", "chunk_order", "make_inputs",
+           "make_ffn_inputs", "chunk_bounds"]

@@ -84,3 +84,27 @@ ALIASES = {
 def get(name: str) -> Workload:
     name = ALIASES.get(name, name)
     return CONFIGS[name]
+
+
+@dataclass(frozen=True)
+class FfnWorkload:
+    """Blockwise feedforward (SwiGLU) of `rows` query rows, `block_rows` at a time."""
+    name: str
+    rows: int
+    d_model: int
+    d_ff: int
+    block_rows: int
+    seed: int = 0
+    description: str = ""
+
+    def flop(self) -> float:
+        # three GEMMs of rows x d_model x d_ff, 2 flop per MAC
+        return 6.0 * self.rows * self.d_model * self.d_ff
+
+
+FFN_CONFIGS = {
+    "ffn_llama2_7b_s32k": FfnWorkload(
+        "ffn_llama2_7b_s32k", 32768, 4096, 11008, 4096,
+        description="Llama-2-7B SwiGLU feedforward (d_model 4096, d_ff 11008) of the 32768 rows of the "
+                    "32K attention workload, in blocks of 4096 rows"),
+}

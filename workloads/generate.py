@@ -41,3 +41,19 @@ def chunk_bounds(seqlen_k, n_chunks):
     """[start, end) of each chunk; equal chunks of ceil(S/n), the last one possibly shorter."""
     c = -(-seqlen_k // n_chunks)
     return [(i * c, min((i + 1) * c, seqlen_k)) for i in range(n_chunks) if i * c < seqlen_k]
+
+
+def make_ffn_inputs(rows, d_model, d_ff, *, seed=0):
+    """Return bf16 CPU tensors (x, w1, w3, w2) for the blockwise feedforward.
+
+    x [rows, d_model] ~ N(0, 1) (activations); the weights are random in the layout of a linear
+    layer ([out, in]) with the usual fan-in scaling, w1, w3 [d_ff, d_model] ~ N(0, 1/d_model) and
+    w2 [d_model, d_ff] ~ N(0, 1/d_ff), so every pre-activation is O(1).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn(rows, d_model, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    w1 = (torch.randn(d_ff, d_model, generator=g, dtype=torch.float32) / d_model ** 0.5).to(torch.bfloat16)
+    w3 = (torch.randn(d_ff, d_model, generator=g, dtype=torch.float32) / d_model ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(d_model, d_ff, generator=g, dtype=torch.float32) / d_ff ** 0.5).to(torch.bfloat16)
+    return x, w1, w3, w2
