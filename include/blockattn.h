@@ -52,7 +52,8 @@ typedef enum {
   BA_OK = 0,
   BA_ERR_NULL = 1,        /* a required pointer is NULL */
   BA_ERR_SHAPE = 2,       /* negative size, heads_q % heads_kv != 0, ... */
-  BA_ERR_STRIDE = 3,      /* a b/s/h stride is negative or not a multiple of 8 elements */
+  BA_ERR_STRIDE = 3,      /* a b/s/h stride is negative or not a multiple of 8 elements,
+                             or a sequence (s) stride is 2^24 elements or more */
   BA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned (lse/delta: 4-byte) */
   BA_ERR_UNSUPPORTED = 5, /* head_dim not in {64, 128}, or an unknown dtype */
   BA_ERR_S2 = 6,          /* invalid S2 layout (see ba_s2_desc) */

@@ -47,6 +47,33 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32 on the vector ALU: v_permlane32_swap
+// exchanges one 32-lane half of its two operands, so with both operands = x the
+// two results hold x of lane l and of lane l ^ 32 (in some order, which a
+// symmetric reduction does not see).  No LDS round trip, unlike a shuffle.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over [base, base + bytes) (raw, stride 0; dword 3 = the gfx9
+// data format used for untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Direct buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// the address is the resource base (scalar registers) plus a per-lane byte
+// offset, so a tile's loads need no per-lane address arithmetic.  As for
+// g2lds16, lane L writes lds_base + 16*L.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, 0, 0, 0);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane L of the wave writes lds_base + 16*L, whatever global address it reads.
 // lds_base must be the same for every lane of the wave.

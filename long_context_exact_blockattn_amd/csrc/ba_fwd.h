@@ -63,7 +63,10 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
   constexpr int KK = D / 16;                 // MFMA k-steps over D
   constexpr int DB = D / 32;                 // 32-wide blocks of D in the output
   constexpr int TILE = BN * D;               // elements per tile
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // K0, V0, K1, V1 (swizzled)
+  // K0, V0, K1, V1 tiles (swizzled), as separate arrays: the compiler then sees
+  // that a direct load into one buffer cannot alias LDS reads of another and
+  // does not wait for the prefetch before reading the current tile.
+  __shared__ __attribute__((aligned(16))) bf16 sK0[TILE], sV0[TILE], sK1[TILE], sV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,12 +144,27 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
     const bf16* kbase = a.k + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
     const bf16* vbase = a.v + (int64_t)b * a.ks_b + (int64_t)kvh * a.ks_h;
     const int ks_s = (int)a.ks_s;
+    unsigned g_off[NPI];  // byte offset of this lane's chunk inside a full tile
+#pragma unroll
+    for (int p = 0; p < NPI; ++p) g_off[p] = 2u * (unsigned)(g_row[p] * ks_s + g_col[p]);
 
     auto issue_tile = [&](bf16* kdst, bf16* vdst, int64_t kt) {
       const KTile t = make_ktile(sc, kt);
       const bf16* kt_base = kbase + t.row0 * a.ks_s;
       const bf16* vt_base = vbase + t.row0 * a.ks_s;
       const int last = (int)t.rows - 1;
+      if (last == BN - 1) {  // full tile: scalar base + the fixed per-lane offsets
+        // the resource spans exactly the tile's rows: (BN - 1) strides plus one row
+        const int bytes = 2 * ((BN - 1) * ks_s + D);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kt_base, bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt_base, bytes);
+#pragma unroll
+        for (int p = 0; p < NPI; ++p) {
+          buf2lds16(krs, g_off[p], kdst + (p * NW + wave) * 512);
+          buf2lds16(vrs, g_off[p], vdst + (p * NW + wave) * 512);
+        }
+        return;
+      }
 #pragma unroll
       for (int p = 0; p < NPI; ++p) {
         const int r = g_row[p] < last ? g_row[p] : last;  // ragged tail re-reads the last row
@@ -204,7 +222,7 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        mx = fmaxf(mx, wave_xor32(mx));
+        mx = halves_max(mx);
         // The running max moves only when a tile's max exceeds it by more than 8
         // (base 2): p = 2^(s - m) then stays <= 256, exact in fp32 sums and in
         // bf16's range, and the O rescale below is skipped on almost every tile.
@@ -243,10 +261,10 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
       }
     };
 
-    bf16* K0 = smem;
-    bf16* V0 = smem + TILE;
-    bf16* K1 = smem + 2 * TILE;
-    bf16* V1 = smem + 3 * TILE;
+    bf16* const K0 = sK0;
+    bf16* const V0 = sV0;
+    bf16* const K1 = sK1;
+    bf16* const V1 = sV1;
     issue_tile(K0, V0, qt.kt_begin);
     wait_vmem();
     __syncthreads();
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
   // ---- epilogue, per query block: partial pair of this chunk, optional merge
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + wave_xor32(l_run[qb]);
+    const float l_tot = halves_sum(l_run[qb]);
     const bool has = l_tot > 0.f;
     const float lse2_c = has ? m_run[qb] + log2_hw(l_tot) : -INFINITY;
     const float inv_l = has ? 1.f / l_tot : 0.f;

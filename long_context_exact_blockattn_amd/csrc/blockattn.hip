@@ -23,6 +23,8 @@ bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 int check_strides(const int64_t s[3]) {
   for (int i = 0; i < 3; ++i)
     if (s[i] < 0 || s[i] % 8 != 0) return BA_ERR_STRIDE;
+  // the kernels address a tile's rows with 32-bit byte offsets from its first row
+  if (s[1] >= ((int64_t)1 << 24)) return BA_ERR_STRIDE;
   return BA_OK;
 }
 

@@ -60,6 +60,8 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, _desc(Sq=-1)) == _lib.BA_ERR_SHAPE
     assert _fwd(lib, _desc(qs=(0, 12, 4))) == _lib.BA_ERR_STRIDE
     assert _fwd(lib, _desc(ks=(0, -8, 8))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(ks=(0, 1 << 24, 8))) == _lib.BA_ERR_STRIDE  # 32-bit tile offsets
+    assert _fwd(lib, _desc(qs=(0, 1 << 24, 8))) == _lib.BA_ERR_STRIDE
     assert _fwd(lib, _desc(), q=FAKE + 2) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), lse=FAKE + 2) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), of=FAKE + 8) == _lib.BA_ERR_ALIGN
