@@ -53,6 +53,7 @@ constexpr int kDqBN = 64;    // key rows per streamed tile
 constexpr int kKvBN = 128;   // keys per dkdv item (4 waves x 32)
 constexpr int kKvBM = 64;    // query rows per streamed tile
 constexpr int kBwdThreads = 256;
+constexpr int kKvThreads = 512;  // dkdv: 4 key blocks x 2 waves
 
 __device__ __forceinline__ Sched bwd_sched(const BwdArgs& a, int head, int BM, int BN) {
   Sched sc;
@@ -66,10 +67,10 @@ __device__ __forceinline__ Sched bwd_sched(const BwdArgs& a, int head, int BM, i
 // Direct loads of one R-row tile into the swizzled LDS layout: slot ci of the
 // tile gets row ci / CPR, chunk (ci % CPR) ^ swz(row) of the source.  Rows past
 // the end of a ragged tile re-read its last valid row (masked by the caller).
-template <int D, int R>
+template <int D, int R, int THREADS = kBwdThreads>
 struct TileLoader {
   static constexpr int CPR = D / 8;
-  static constexpr int NW = kBwdThreads / 64;
+  static constexpr int NW = THREADS / 64;
   static constexpr int NPI = R * CPR / (64 * NW);
   static constexpr int STEP = 64 * NW / CPR;  // rows between consecutive instructions
   // Slot ci = (p*NW + wave)*64 + lane is row ci / CPR = row0 + p*STEP; the row's
@@ -94,7 +95,8 @@ struct TileLoader {
 #endif
   }
 };
-static_assert(TileLoader<128, 64>::STEP % 16 == 0 && TileLoader<64, 64>::STEP % 16 == 0,
+static_assert(TileLoader<128, 64>::STEP % 16 == 0 && TileLoader<64, 64>::STEP % 16 == 0 &&
+                  TileLoader<128, 64, kKvThreads>::STEP % 16 == 0 && TileLoader<64, 64, kKvThreads>::STEP % 16 == 0,
               "the loader assumes the swizzle repeats every STEP rows");
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -290,19 +292,35 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV (key/value-stationary)
+// Eight waves: each 32-key block of the item is owned by a PAIR of waves that
+// share a SIMD.  The P wave holds K and computes S, P = exp(S - LSE) and
+// dV += P^T dO; the dS wave holds V and computes dP = dO V^T, dS = P (dP -
+// delta) and dK += dS^T Q, taking P from the P wave through LDS (fp32, in the
+// accumulator layout both waves share: lane = key, register = query).  A tile
+// of 64 query rows runs in two phases separated by a barrier: scores / dP
+// MFMAs and the P softmax, then the two gradient contractions.  Each wave
+// keeps one stationary operand and one accumulator set, so two waves fit on
+// a SIMD and each one's VALU work runs under the other's MFMAs.
 template <int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = kKvBM, BN = kKvBN;
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = BM * D;
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // Q0, dO0, Q1, dO1 (swizzled)
+  constexpr int NKB = BN / 32;  // key blocks = wave pairs
+  // two buffers, each a Q tile followed by a dO tile (swizzled); separate arrays
+  // so prefetches into one buffer do not make the compiler wait before reading
+  // the other
+  __shared__ __attribute__((aligned(16))) bf16 sT0[2 * TILE], sT1[2 * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse*log2e, delta][row]
+  __shared__ __attribute__((aligned(16))) f32x4 pbuf[NKB][2][4][64];  // [key block][qb][quarter][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
+  const int kblk = wave % NKB;
+  const bool pwave = wave < NKB;  // P / dV wave; otherwise dP / dS / dK wave
 
   const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
   const int64_t bkv = pid / a.n_tiles;
@@ -313,23 +331,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const Sched sc = bwd_sched(a, h0, BM, BN);  // every head of the group shares the shift
   const KVItem it = make_kv_item(sc, ktile_of_rank(sc, a.n_tiles, w));
 
-  const int kloc = wave * 32 + l32;
+  const int kloc = kblk * 32 + l32;
   const bool key_ok = kloc < it.krows;
   const int64_t krow = it.krow0 + kloc;
   const int64_t kcpos = it.kcpos0 + kloc;
-  const int64_t wave_kmin = it.kcpos0 + wave * 32;
+  const int64_t wave_kmin = it.kcpos0 + kblk * 32;
   const int64_t wave_kmax = wave_kmin + 31;
   const int64_t koff = (int64_t)b * a.ks_b + krow * a.ks_s + (int64_t)kvh * a.ks_h;
 
-  bf16x8 kf[KK], vf[KK];
+  // stationary operand: K rows (P wave) or V rows (dS wave)
+  bf16x8 sf[KK];
+  {
+    const bf16* src = pwave ? a.k : a.v;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    kf[kk] = key_ok ? *(const bf16x8*)(a.k + koff + 16 * kk + 8 * hl) : bf16x8{};
-    vf[kk] = key_ok ? *(const bf16x8*)(a.v + koff + 16 * kk + 8 * hl) : bf16x8{};
+    for (int kk = 0; kk < KK; ++kk)
+      sf[kk] = key_ok ? *(const bf16x8*)(src + koff + 16 * kk + 8 * hl) : bf16x8{};
   }
-  f32x16 dkacc[DB], dvacc[DB];
+  f32x16 acc[DB];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   const int64_t nqt = it.qt_end > it.qt_begin ? it.qt_end - it.qt_begin : 0;
   const int64_t n_iter = nqt * a.grp;
@@ -346,102 +366,133 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       t_off[db][0] = tile_off<D>(r0, dcol);
       t_off[db][1] = tile_off<D>(r0 + 8, dcol);
     }
-    TileLoader<D, BM> ld;
+    TileLoader<D, BM, kKvThreads> ld;
     ld.init(wave, lane);
     const int qs_s = (int)a.qs_s;
     auto tile_of = [&](int64_t i, int* head, QTile* t) {
       *head = h0 + (int)(i / nqt);
       *t = make_qtile(sc, it.qt_begin + i % nqt);
     };
-    // stage tile i: Q and dO by direct loads, LSE (base 2) and delta by ordinary loads
+    // stage tile i: LSE and delta by ordinary loads (issued first, consumed only
+    // after the tile in flight has been processed), Q and dO by direct loads
     float st_l = INFINITY, st_d = 0.f;
+    bool st_ok = false;
     auto issue = [&](bf16* qd, bf16* dd, int64_t i) {
       int hh; QTile t; tile_of(i, &hh, &t);
+      if (tid < BM) {
+        st_ok = tid < t.rows;
+        const int64_t li = ((int64_t)b * a.Hq + hh) * a.Sq + t.row0 + (st_ok ? tid : 0);
+        st_l = a.lse[li];
+        st_d = a.delta[li];
+      }
       const int64_t base = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
       ld.issue(a.q + base, qs_s, (int)t.rows, qd, wave);
       ld.issue(a.dout + base, qs_s, (int)t.rows, dd, wave);
-      if (tid < BM) {
-        const bool ok = tid < t.rows;
-        const int64_t li = ((int64_t)b * a.Hq + hh) * a.Sq + t.row0 + tid;
-        st_l = ok ? a.lse[li] * kLog2e : INFINITY;
-        st_d = ok ? a.delta[li] : 0.f;
-      }
     };
     auto put_stats = [&](int buf) {
       if (tid < BM) {
-        stat[buf][0][tid] = st_l;
-        stat[buf][1][tid] = st_d;
+        stat[buf][0][tid] = st_ok ? st_l * kLog2e : INFINITY;
+        stat[buf][1][tid] = st_ok ? st_d : 0.f;
       }
     };
 
-    auto tile_step = [&](const bf16* Qs, const bf16* Ds, const float* lse_s, const float* del_s, int64_t i) {
+    // QDs: one buffer, the Q tile followed by the dO tile
+    auto tile_step = [&](const bf16* QDs, const float* lse_s, const float* del_s, int64_t i) {
       int hh; QTile t; tile_of(i, &hh, &t);
+      bool act[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) act[qb] = !(a.causal && wave_kmin > t.cpos0 + qb * 32 + 31);
+      // ---- phase 1: S^T = K Q^T (P wave) or dP^T = V dO^T (dS wave), 32 queries per block
+      const bf16* Xs = QDs + (pwave ? 0 : TILE);
+      f32x16 x[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int64_t qc0 = t.cpos0 + qb * 32;
-        if (a.causal && wave_kmin > qc0 + 31) continue;  // every pair of the block is masked
-        const bool need_mask = (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > qc0);
-        // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
-        int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
-        if (need_mask) {
-          if (!key_ok) {
-            qmin = 64;
-          } else if (a.causal) {
-            int64_t c = kcpos - qc0;
-            c = c < -1 ? -1 : (c > 64 ? 64 : c);
-            qmin = (int)c;
+        if (!act[qb]) continue;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          x[qb] = mfma32(*(const bf16x8*)(Xs + qb * 32 * D + n_off[kk]), sf[kk], kk == 0 ? f32x16{} : x[qb]);
+      }
+      bf16x8 pf[2][2];
+      if (pwave) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!act[qb]) continue;
+          const int64_t qc0 = t.cpos0 + qb * 32;
+          const bool need_mask = (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > qc0);
+          // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
+          int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
+          if (need_mask) {
+            if (!key_ok) {
+              qmin = 64;
+            } else if (a.causal) {
+              int64_t c = kcpos - qc0;
+              c = c < -1 ? -1 : (c > 64 ? 64 : c);
+              qmin = (int)c;
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *(const f32x4*)(lse_s + qb * 32 + 8 * g + 4 * hl);
+            f32x4 p4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float p = exp2_hw(__builtin_fmaf(x[qb][r], a.scale_log2, -l4[e]));
+              if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
+              p4[e] = p;
+              pf[qb][r >> 3][r & 7] = (bf16)p;
+            }
+            pbuf[kblk][qb][g][lane] = p4;
           }
         }
-        f32x16 s, dp;
+      }
+      // P of this tile is in LDS; the prefetch of the next tile stays in flight
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // ---- phase 2: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
+      // transposed operand is read from the [query][d] tile
+      const bf16* Ys = QDs + (pwave ? TILE : 0);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          s = mfma32(*(const bf16x8*)(Qs + qb * 32 * D + n_off[kk]), kf[kk], kk == 0 ? f32x16{} : s);
-          dp = mfma32(*(const bf16x8*)(Ds + qb * 32 * D + n_off[kk]), vf[kk], kk == 0 ? f32x16{} : dp);
-        }
-        bf16x8 pf[2], dsf[2];
+      for (int qb = 0; qb < 2; ++qb) {
+        if (!act[qb]) continue;
+        bf16x8 yf[2];
+        if (pwave) {
+          yf[0] = pf[qb][0];
+          yf[1] = pf[qb][1];
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int q4 = qb * 32 + 8 * g + 4 * hl;
-          const f32x4 l4 = *(const f32x4*)(lse_s + q4);
-          const f32x4 d4 = *(const f32x4*)(del_s + q4);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 p4 = pbuf[kblk][qb][g][lane];
+            const f32x4 d4 = *(const f32x4*)(del_s + qb * 32 + 8 * g + 4 * hl);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -l4[e]));
-            if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
-            pf[r >> 3][r & 7] = (bf16)p;
-            dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - d4[e]));
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              yf[r >> 3][r & 7] = (bf16)(p4[e] * (x[qb][r] - d4[e]));
+            }
           }
         }
-        // dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             const int rb = (qb * 32 + 16 * c2) * D;
-            dvacc[db] = mfma32(tr_pair(Ds + rb, t_off[db][0], t_off[db][1]), pf[c2], dvacc[db]);
-            dkacc[db] = mfma32(tr_pair(Qs + rb, t_off[db][0], t_off[db][1]), dsf[c2], dkacc[db]);
+            acc[db] = mfma32(tr_pair(Ys + rb, t_off[db][0], t_off[db][1]), yf[c2], acc[db]);
           }
       }
     };
 
-    bf16* Q0 = smem;
-    bf16* D0 = smem + TILE;
-    bf16* Q1 = smem + 2 * TILE;
-    bf16* D1 = smem + 3 * TILE;
-    issue(Q0, D0, 0);
+    issue(sT0, sT0 + TILE, 0);
     put_stats(0);
     wait_vmem();
     __syncthreads();
     for (int64_t i = 0; i < n_iter; i += 2) {
-      if (i + 1 < n_iter) issue(Q1, D1, i + 1);
-      tile_step(Q0, D0, stat[0][0], stat[0][1], i);
+      if (i + 1 < n_iter) issue(sT1, sT1 + TILE, i + 1);
+      tile_step(sT0, stat[0][0], stat[0][1], i);
       if (i + 1 < n_iter) put_stats(1);
       wait_vmem();
       __syncthreads();
       if (i + 1 >= n_iter) break;
-      if (i + 2 < n_iter) issue(Q0, D0, i + 2);
-      tile_step(Q1, D1, stat[1][0], stat[1][1], i + 1);
+      if (i + 2 < n_iter) issue(sT0, sT0 + TILE, i + 2);
+      tile_step(sT1, stat[1][0], stat[1][1], i + 1);
       if (i + 2 < n_iter) put_stats(0);
       wait_vmem();
       __syncthreads();
@@ -450,26 +501,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   if (!key_ok) return;
   const int64_t obase = koff + 4 * hl;
+  void* const dst = pwave ? a.dv : a.dk;
+  const float mul = pwave ? 1.f : a.scale;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t off = obase + 32 * db + 8 * g;
-      f32x4 kv4, vv4;
+      f32x4 v4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv4[e] = a.scale * dkacc[db][4 * g + e];
-        vv4[e] = dvacc[db][4 * g + e];
-      }
+      for (int e = 0; e < 4; ++e) v4[e] = mul * acc[db][4 * g + e];
       if (a.dkv_f32) {
-        *(f32x4*)((float*)a.dk + off) = kv4;
-        *(f32x4*)((float*)a.dv + off) = vv4;
+        *(f32x4*)((float*)dst + off) = v4;
       } else {
-        bf16x4 kb4, vb4;
+        bf16x4 b4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { kb4[e] = (bf16)kv4[e]; vb4[e] = (bf16)vv4[e]; }
-        *(bf16x4*)((bf16*)a.dk + off) = kb4;
-        *(bf16x4*)((bf16*)a.dv + off) = vb4;
+        for (int e = 0; e < 4; ++e) b4[e] = (bf16)v4[e];
+        *(bf16x4*)((bf16*)dst + off) = b4;
       }
     }
   }

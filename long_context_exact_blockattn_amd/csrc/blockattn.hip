@@ -161,9 +161,9 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
     b.n_items = (int64_t)d->batch * d->heads_kv * b.n_tiles;
     if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
     if (d128)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)b.n_items), dim3(kKvThreads), 0, stream, b);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)b.n_items), dim3(kKvThreads), 0, stream, b);
     if ((r = launched())) return r;
   }
   if (d->seqlen_q > 0) {
