@@ -62,16 +62,16 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 // Buffer resource over [base, base + bytes) (raw, stride 0; dword 3 = the gfx9
 // data format used for untyped loads).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Direct buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
 // the address is the resource base (scalar registers) plus a per-lane byte
-// offset, so a tile's loads need no per-lane address arithmetic.  As for
-// g2lds16, lane L writes lds_base + 16*L.
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, 0, 0, 0);
+// offset (plus a scalar offset), so a tile's loads need no per-lane address
+// arithmetic.  As for g2lds16, lane L writes lds_base + 16*L.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff, 0, 0);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
@@ -98,6 +98,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 template <int D>
 BA_HD int swz(int r) {
   if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if (D == 32) return (r >> 2) & 3;  // 4 chunks, 16 banks per row: 16-byte reads only
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);  // D == 64: 8 chunks, 32 banks per row
 }
 

@@ -40,6 +40,7 @@ struct GemmArgs {
 constexpr int kGemmThreads = 512;
 constexpr int kGemmBM = 256;
 constexpr int kGemmBK = 64;
+constexpr int kGemmGroupM = 4;
 
 template <int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt_kernel(GemmArgs g) {
@@ -59,9 +60,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt_kernel(GemmArgs g) {
   const int wm = wave & 3, wn = wave >> 2;
   const int hl = lane >> 5, l32 = lane & 31;
 
+  // Item order: groups of kGemmGroupM row tiles, each group walking every
+  // column tile; with the XCD remap the 32 items an XCD runs at once span 4 row
+  // tiles x 8 column tiles, so their A and B slices are shared in that XCD's L2
+  // (the kernel is bound by L2-miss traffic into LDS, not by the matrix cores).
   const int64_t item = xcd_remap(blockIdx.x, g.n_items);
-  const int tn = (int)(item / g.tiles_m);
-  const int64_t m0 = (item % g.tiles_m) * BM;
+  const int64_t per_group = (int64_t)kGemmGroupM * g.tiles_n;
+  const int64_t first_m = (item / per_group) * kGemmGroupM;
+  const int gsz = (int)((g.tiles_m - first_m) < kGemmGroupM ? (g.tiles_m - first_m) : kGemmGroupM);
+  const int64_t within = item % per_group;
+  const int tn = (int)(within / gsz);
+  const int64_t m0 = (first_m + within % gsz) * BM;
   const int n0 = tn * (EPI == EPI_SWIGLU ? 128 : 256);  // first output column of the item
 
   // loader: thread slot ci = (p*NW + wave)*64 + lane holds tile row ci / CPR
@@ -70,7 +79,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt_kernel(GemmArgs g) {
   // 32-bit element offsets from uniform bases (the host keeps every operand
   // under 2^31 elements)
   unsigned a_src[NPI], b_src[NPI];
-  const bf16* b_base[NPI];
 #pragma unroll
   for (int p = 0; p < NPI; ++p) {
     const int r = ld_row0 + p * STEP;
@@ -80,18 +88,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_nt_kernel(GemmArgs g) {
     if (EPI == EPI_SWIGLU) {
       // ld_row0 < 64 = STEP, so row r is in 64-row group p: W1 for even p, W3 for odd,
       // output columns n0 + 64 (p / 2) + ld_row0
-      b_base[p] = (p & 1) ? g.b3 : g.b;
       b_src[p] = (unsigned)((int64_t)(n0 + 64 * (p >> 1) + ld_row0) * g.K + ld_col);
     } else {
-      b_base[p] = g.b;
       b_src[p] = (unsigned)((int64_t)(n0 + r) * g.K + ld_col);
     }
   }
+  // buffer loads: scalar bases, per-lane byte offsets fixed for the item and
+  // the K position in the scalar offset (the host keeps every operand under
+  // 2^31 elements, so byte offsets fit in 32 bits)
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t rb3 = make_rsrc(EPI == EPI_SWIGLU ? g.b3 : g.b, 0xFFFFFFFFu);
   auto issue = [&](bf16* sa, bf16* sb, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NPI; ++p) {
-      g2lds16(g.a + (a_src[p] + k0), sa + (p * NW + wave) * 512);
-      g2lds16(b_base[p] + (b_src[p] + k0), sb + (p * NW + wave) * 512);
+      buf2lds16(ra, 2u * a_src[p], 2u * k0, sa + (p * NW + wave) * 512);
+      buf2lds16((EPI == EPI_SWIGLU && (p & 1)) ? rb3 : rb, 2u * b_src[p], 2u * k0, sb + (p * NW + wave) * 512);
     }
   };
 

@@ -155,13 +155,13 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
       const int last = (int)t.rows - 1;
       if (last == BN - 1) {  // full tile: scalar base + the fixed per-lane offsets
         // the resource spans exactly the tile's rows: (BN - 1) strides plus one row
-        const int bytes = 2 * ((BN - 1) * ks_s + D);
+        const unsigned bytes = 2u * (unsigned)((BN - 1) * ks_s + D);
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kt_base, bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt_base, bytes);
 #pragma unroll
         for (int p = 0; p < NPI; ++p) {
-          buf2lds16(krs, g_off[p], kdst + (p * NW + wave) * 512);
-          buf2lds16(vrs, g_off[p], vdst + (p * NW + wave) * 512);
+          buf2lds16(krs, g_off[p], 0u, kdst + (p * NW + wave) * 512);
+          buf2lds16(vrs, g_off[p], 0u, vdst + (p * NW + wave) * 512);
         }
         return;
       }
