@@ -140,8 +140,9 @@ def side_measurements(w, tensors, reps=5):
     ms_d = _event_ms(delta_only, reps)
     bytes_d = elems * (2 + 2) + rows * 4
     # Ulysses layout permutes at one device's share of this workload on 8 devices (S/8 rows, all
-    # heads): every element read once and written once
-    n_dev = 8
+    # heads; fewer devices when the heads do not split 8 ways): every element read once and
+    # written once
+    n_dev = max(n for n in range(1, 9) if w.heads_q % n == 0)
     x_share = q[:, : s // n_dev].contiguous()
     send = _lib.ulysses_pack(x_share, n_dev)
     ms_pack = _event_ms(lambda: _lib.ulysses_pack(x_share, n_dev, send=send), reps * 4)
@@ -152,6 +153,8 @@ def side_measurements(w, tensors, reps=5):
                          ("ulysses_pack", ms_pack, bytes_u), ("ulysses_unpack", ms_unpack, bytes_u)):
         gbs = by / (ms * 1e-3) / 1e9
         hbm[name] = {"bytes": by, "ms": round(ms, 4), "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        if name.startswith("ulysses"):
+            hbm[name]["n_devices"] = n_dev
     res["hbm_kernels"] = hbm
 
     # the ring's receive side: each step's chunk copied into one of two staging buffers on a

@@ -259,8 +259,10 @@ def ulysses_pack(x, n_devices, *, send=None, stream=None):
     import torch
     _dense_bf16(x, "x", "ulysses_pack")
     b, sl, h, d = x.shape
+    if n_devices < 1 or h % n_devices != 0:
+        raise BlockAttnError(BA_ERR_SHAPE, "ulysses_pack (heads must split evenly over n_devices)")
     if send is None:
-        send = torch.empty((n_devices, b, sl, h // max(n_devices, 1), d), device=x.device, dtype=x.dtype)
+        send = torch.empty((n_devices, b, sl, h // n_devices, d), device=x.device, dtype=x.dtype)
     _dense_bf16(send, "send", "ulysses_pack")
     if send.numel() != x.numel():
         raise BlockAttnError(BA_ERR_SHAPE, "ulysses_pack (send must hold as many elements as x)")

@@ -46,6 +46,17 @@ def ring_forward(q, k, v, n_chunks, order=None, *, causal=True, scale=None, o_ac
     return out, lse, o_acc
 
 
+_COPY_STREAMS = {}  # device index -> the side stream staged rings copy on (created once)
+
+
+def _copy_stream(device):
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _COPY_STREAMS:
+        _COPY_STREAMS[idx] = torch.cuda.Stream(device=idx)  # default priority
+    return _COPY_STREAMS[idx]
+
+
 def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=None, copy_stream=None):
     """ring_forward with every step's key/value chunk first copied into one of two staging buffers
     on a second stream, the copy for step t+1 running while step t computes.
@@ -55,7 +66,8 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
     and the method has no overhead when the compute of a step outlasts the transfer of a block.
     Here the transfer is a device-to-device copy of the same bytes.  The compute of step t waits
     for the copy of its chunk (event); the copy into a staging buffer waits for the compute that
-    last read it (event), so the two buffers alternate.  Both streams have the default priority.
+    last read it (event), so the two buffers alternate.  Both streams have the default priority;
+    without copy_stream the copies run on one side stream per device, created on first use.
     Returns (out bf16, lse fp32, o_acc fp32), equal bit for bit to ring_forward's.
     """
     bounds = _bounds(k.shape[1], n_chunks)
@@ -64,7 +76,7 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
         raise ValueError("order must be a permutation of the chunk indices")
     b, s, hq, d = q.shape
     main = torch.cuda.current_stream(q.device)
-    side = torch.cuda.Stream(device=q.device) if copy_stream is None else copy_stream
+    side = _copy_stream(q.device) if copy_stream is None else copy_stream
     cmax = max(c1 - c0 for c0, c1 in bounds)
     kbuf = [torch.empty(b, cmax, k.shape[2], d, device=k.device, dtype=k.dtype) for _ in range(2)]
     vbuf = [torch.empty(b, cmax, v.shape[2], d, device=v.device, dtype=v.dtype) for _ in range(2)]
