@@ -59,6 +59,16 @@ def test_backward_ring_chunks(n_chunks, S):
         _check_grads(f"bwd ring n={n_chunks} S={S} order={order}", got, ref)
 
 
+def test_backward_bitwise_deterministic():
+    """No atomics anywhere in the backward: two runs on the same inputs agree bit for bit."""
+    q, k, v, do = make_inputs(1, 1500, 4, 2, 128, seed=97, with_dout=True)
+    order = chunk_order(3, seed=1)
+    first = _gpu_forward_backward(q, k, v, do, 3, order)
+    second = _gpu_forward_backward(q, k, v, do, 3, order)
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
+
+
 def test_backward_fp32_dkdv_and_batch():
     B, S, H, D = 2, 400, 2, 128
     q, k, v, do = make_inputs(B, S, H, H, D, seed=95, with_dout=True)

@@ -26,8 +26,10 @@ def _check(tag, got, ref):
     assert err <= TOL_FFN and amax <= np.abs(ref).max() / 64
 
 
+# (1300, ..., 1300): six row tiles, so the item order's groups of four row tiles end in a
+# partial group of two
 @pytest.mark.parametrize("rows,d_model,d_ff,block_rows", [(1000, 256, 384, 300), (256, 512, 128, 256),
-                                                          (77, 256, 256, 1000)])
+                                                          (77, 256, 256, 1000), (1300, 256, 384, 1300)])
 def test_ffn_small(rows, d_model, d_ff, block_rows):
     x, w1, w3, w2 = make_ffn_inputs(rows, d_model, d_ff, seed=rows)
     out = ba.bpt_ffn(*(t.to(dev()) for t in (x, w1, w3, w2)), block_rows=block_rows)
