@@ -396,11 +396,11 @@ def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
         "workload": "llama2_7b_s32k_ring8 (8 ring steps, one dispatch each)",
         "kernel_source_sha": _src_sha(FWD_SRC),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_copy_fetch -o cfetch -- python -u bench.py --copy-calibration --steps 3",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_copy_write -o cwrite -- python -u bench.py --copy-calibration --steps 3",
-            "python bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write",
+            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
+            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
+            f"rocprofv3 --pmc FETCH_SIZE -d {copy_fetch_dir} -o cfetch -- python -u bench.py --copy-calibration --steps 3",
+            f"rocprofv3 --pmc WRITE_SIZE -d {copy_write_dir} -o cwrite -- python -u bench.py --copy-calibration --steps 3",
+            f"python bench.py --traffic-summary {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}",
         ],
         "copy_calibration": {"bytes_per_copy": n, "fetch_size_kib": max(cf), "write_size_kib": max(cw),
                              "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
