@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_BASIS = "256 CUs x 4096 bf16 flop/clk (dense MFMA) x 2.4 GHz peak engine clock; HBM 8 TB/s"
 PEAK_HBM_GBS = 8000.0
 METRIC = "causal attention fwd/bwd TFLOP/s and % bf16 MFMA peak at S=32K-128K, D=128"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -86,10 +87,27 @@ def run_ring_forward(w, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [ev[i][t].elapsed_time(ev[i][t + 1]) for i in range(steps) for t in range(n)]
+    step_ms = [ev[i][0].elapsed_time(ev[i][n]) for i in range(steps)]
     assert not torch.isnan(out).any(), "NaN in output"
-    return {"wall_s": wall, "launch_ms": launch_ms, "launches_per_step": n, "order": order,
+    return {"wall_s": wall, "launch_ms": launch_ms, "step_ms": step_ms, "launches_per_step": n, "order": order,
             "kernel": f"fwd_kernel<{w.head_dim}>", "src": FWD_SRC,
             "tensors": (q, k, v, o_acc, lse, out)}
+
+
+def _stats(xs):
+    import statistics
+    return {"median": round(statistics.median(xs), 4), "min": round(min(xs), 4), "max": round(max(xs), 4)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 def _event_ms(fn, reps):
@@ -239,22 +257,19 @@ def run_training(w, steps, warmup):
                 _lib.blockattn_bwd(q, k[:, c0:c1], v[:, c0:c1], o, do, lse, delta, dq_acc,
                                    dk[:, c0:c1], dv[:, c0:c1], dq_final=dq, flags=flags, k_pos0=c0)
 
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for _ in range(warmup):
         fwd(); bwd()
     torch.cuda.synchronize()
-    fwd_ms, bwd_ms = [], []
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for e in ev:
         e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for _ in range(steps):
-        pass
-    fwd_ms = e[0].elapsed_time(e[1])
-    bwd_ms = e[1].elapsed_time(e[2])
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
     assert not torch.isnan(dq).any() and not torch.isnan(dk).any(), "NaN in gradients"
-    return {"wall_s": wall, "fwd_ms_last": fwd_ms, "bwd_ms_last": bwd_ms, "order": order}
+    return {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "order": order}
 
 
 def cpu_baseline(w, budget_heads=1):
@@ -282,7 +297,10 @@ def cpu_baseline(w, budget_heads=1):
     flop = w.fwd_flop() * len(heads) / w.heads_q
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{w.name}: query head 0 of {w.heads_q} at full S={w.seqlen}, all {w.n_chunks} ring "
-                      f"steps in the seeded order, numpy float64; {dt:.1f} s for {flop:.3e} algorithmic flop"}
+                      f"steps in the seeded order, numpy float64; {dt:.1f} s for {flop:.3e} algorithmic flop",
+            "seconds": round(dt, 3),
+            "extrapolated_full_config_s": round(dt * w.heads_q / len(heads), 1),
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
 
 
 def copy_calibration(reps):
@@ -487,8 +505,10 @@ def ffn_line(w, args):
 
 def training_line(w, args):
     """One JSON line for a forward+backward workload (attention training step)."""
+    import statistics
     r = run_training(w, args.steps, args.warmup)
     ms = r["wall_s"] * 1e3 / args.steps
+    fwd_med, bwd_med = statistics.median(r["fwd_ms"]), statistics.median(r["bwd_ms"])
     flop = w.fwd_flop() + w.bwd_flop()
     tflops = flop / (ms * 1e-3) / 1e12
     line = {
@@ -500,9 +520,12 @@ def training_line(w, args):
                    "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks,
                    "s2_group": w.s2_group, "chunk_order": r["order"], "phases": "forward+backward",
                    "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                   "fwd_ms": round(r["fwd_ms_last"], 4), "bwd_ms": round(r["bwd_ms_last"], 4),
-                   "fwd_tflops": round(w.fwd_flop() / r["fwd_ms_last"] / 1e9, 2),
-                   "bwd_tflops": round(w.bwd_flop() / r["bwd_ms_last"] / 1e9, 2)},
+                   # medians of per-step HIP-event times of each phase
+                   "fwd_ms": round(fwd_med, 4), "bwd_ms": round(bwd_med, 4),
+                   "fwd_tflops": round(w.fwd_flop() / fwd_med / 1e9, 2),
+                   "bwd_tflops": round(w.bwd_flop() / bwd_med / 1e9, 2)},
+        "step_ms": {"fwd": _stats(r["fwd_ms"]), "bwd": _stats(r["bwd_ms"])},
+        "peak_basis": PEAK_BASIS,
     }
     print(json.dumps(line), flush=True)
 
@@ -572,6 +595,9 @@ def main():
                    "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks,
                    "chunk_order": r["order"], "causal": True, "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": roofline,
+        # per-step HIP-event times on the working stream (the value above is from the wall clock)
+        "step_ms": _stats(r["step_ms"]),
+        "peak_basis": PEAK_BASIS,
     }
     tensors = r.pop("tensors")
     if not args.no_side_measurements:
