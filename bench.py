@@ -533,7 +533,7 @@ def training_line(w, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=120)  # about 1 s of timed work on the headline workload
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_7b_s32k_ring8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
