@@ -369,16 +369,27 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     TileLoader<D, BM, kKvThreads> ld;
     ld.init(wave, lane);
     const int qs_s = (int)a.qs_s;
-    auto tile_of = [&](int64_t i, int* head, QTile* t) {
-      *head = h0 + (int)(i / nqt);
-      *t = make_qtile(sc, it.qt_begin + i % nqt);
+    // tiles run over the group's heads, each over the query tiles [qt_begin, qt_end); the
+    // loads and the compute each keep their own position (no divisions per tile)
+    struct Pos {
+      int head;
+      int64_t qtile;
     };
+    auto advance = [&](Pos& p) {
+      if (++p.qtile == it.qt_end) {
+        p.qtile = it.qt_begin;
+        ++p.head;
+      }
+    };
+    Pos pos_load{h0, it.qt_begin}, pos_comp{h0, it.qt_begin};
     // stage tile i: LSE and delta by ordinary loads (issued first, consumed only
     // after the tile in flight has been processed), Q and dO by direct loads
     float st_l = INFINITY, st_d = 0.f;
     bool st_ok = false;
-    auto issue = [&](bf16* qd, bf16* dd, int64_t i) {
-      int hh; QTile t; tile_of(i, &hh, &t);
+    auto issue = [&](bf16* qd, bf16* dd) {
+      const int hh = pos_load.head;
+      const QTile t = make_qtile(sc, pos_load.qtile);
+      advance(pos_load);
       if (tid < BM) {
         st_ok = tid < t.rows;
         const int64_t li = ((int64_t)b * a.Hq + hh) * a.Sq + t.row0 + (st_ok ? tid : 0);
@@ -397,20 +408,33 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     };
 
     // QDs: one buffer, the Q tile followed by the dO tile
-    auto tile_step = [&](const bf16* QDs, const float* lse_s, const float* del_s, int64_t i) {
-      int hh; QTile t; tile_of(i, &hh, &t);
+    auto tile_step = [&](const bf16* QDs, const float* lse_s, const float* del_s) {
+      const QTile t = make_qtile(sc, pos_comp.qtile);
+      advance(pos_comp);
       bool act[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) act[qb] = !(a.causal && wave_kmin > t.cpos0 + qb * 32 + 31);
       // ---- phase 1: S^T = K Q^T (P wave) or dP^T = V dO^T (dS wave), 32 queries per block
+      // (fragments read one pair of k-steps ahead of the MFMAs that use them)
       const bf16* Xs = QDs + (pwave ? 0 : TILE);
       f32x16 x[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (!act[qb]) continue;
+        bf16x8 fr[2][2];
+        auto rd = [&](int kk2, int set) __attribute__((always_inline)) {
+          fr[set][0] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2]);
+          fr[set][1] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2 + 1]);
+        };
+        rd(0, 0);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          x[qb] = mfma32(*(const bf16x8*)(Xs + qb * 32 * D + n_off[kk]), sf[kk], kk == 0 ? f32x16{} : x[qb]);
+        for (int kk2 = 0; kk2 < KK / 2; ++kk2) {
+          if (kk2 + 1 < KK / 2) rd(kk2 + 1, (kk2 + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          x[qb] = mfma32(fr[kk2 & 1][0], sf[2 * kk2], kk2 == 0 ? f32x16{} : x[qb]);
+          x[qb] = mfma32(fr[kk2 & 1][1], sf[2 * kk2 + 1], x[qb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       bf16x8 pf[2][2];
       if (pwave) {
@@ -470,29 +494,36 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             }
           }
         }
+        // transposed fragments read one step ahead of their MFMAs
+        bf16x8 tf[2];
+        auto rdt = [&](int j) __attribute__((always_inline)) {
+          const int db = j >> 1, c2 = j & 1;
+          tf[j & 1] = tr_pair(Ys + (qb * 32 + 16 * c2) * D, t_off[db][0], t_off[db][1]);
+        };
+        rdt(0);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const int rb = (qb * 32 + 16 * c2) * D;
-            acc[db] = mfma32(tr_pair(Ys + rb, t_off[db][0], t_off[db][1]), yf[c2], acc[db]);
-          }
+        for (int j = 0; j < 2 * DB; ++j) {
+          if (j + 1 < 2 * DB) rdt(j + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[j >> 1] = mfma32(tf[j & 1], yf[j & 1], acc[j >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     };
 
-    issue(sT0, sT0 + TILE, 0);
+    issue(sT0, sT0 + TILE);
     put_stats(0);
     wait_vmem();
     __syncthreads();
     for (int64_t i = 0; i < n_iter; i += 2) {
-      if (i + 1 < n_iter) issue(sT1, sT1 + TILE, i + 1);
-      tile_step(sT0, stat[0][0], stat[0][1], i);
+      if (i + 1 < n_iter) issue(sT1, sT1 + TILE);
+      tile_step(sT0, stat[0][0], stat[0][1]);
       if (i + 1 < n_iter) put_stats(1);
       wait_vmem();
       __syncthreads();
       if (i + 1 >= n_iter) break;
-      if (i + 2 < n_iter) issue(sT0, sT0 + TILE, i + 2);
-      tile_step(sT1, stat[1][0], stat[1][1], i + 1);
+      if (i + 2 < n_iter) issue(sT0, sT0 + TILE);
+      tile_step(sT1, stat[1][0], stat[1][1]);
       if (i + 2 < n_iter) put_stats(0);
       wait_vmem();
       __syncthreads();
