@@ -418,9 +418,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       // (fragments read one pair of k-steps ahead of the MFMAs that use them)
       const bf16* Xs = QDs + (pwave ? 0 : TILE);
       f32x16 x[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (!act[qb]) continue;
+      auto contract = [&](int qb) __attribute__((always_inline)) {
         bf16x8 fr[2][2];
         auto rd = [&](int kk2, int set) __attribute__((always_inline)) {
           fr[set][0] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2]);
@@ -430,44 +428,65 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk2 = 0; kk2 < KK / 2; ++kk2) {
           if (kk2 + 1 < KK / 2) rd(kk2 + 1, (kk2 + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
           x[qb] = mfma32(fr[kk2 & 1][0], sf[2 * kk2], kk2 == 0 ? f32x16{} : x[qb]);
           x[qb] = mfma32(fr[kk2 & 1][1], sf[2 * kk2 + 1], x[qb]);
-          __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      };
+      // P = exp(S - LSE) of block qb (zero where masked), to LDS for the dS wave and
+      // as bf16 operands for dV
       bf16x8 pf[2][2];
-      if (pwave) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!act[qb]) continue;
-          const int64_t qc0 = t.cpos0 + qb * 32;
-          const bool need_mask = (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > qc0);
-          // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
-          int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
-          if (need_mask) {
-            if (!key_ok) {
-              qmin = 64;
-            } else if (a.causal) {
-              int64_t c = kcpos - qc0;
-              c = c < -1 ? -1 : (c > 64 ? 64 : c);
-              qmin = (int)c;
-            }
+      auto softmax = [&](int qb, bool need_mask) __attribute__((always_inline)) {
+        const int64_t qc0 = t.cpos0 + qb * 32;
+        // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
+        int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
+        if (need_mask) {
+          if (!key_ok) {
+            qmin = 64;
+          } else if (a.causal) {
+            int64_t c = kcpos - qc0;
+            c = c < -1 ? -1 : (c > 64 ? 64 : c);
+            qmin = (int)c;
           }
+        }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *(const f32x4*)(lse_s + qb * 32 + 8 * g + 4 * hl);
-            f32x4 p4;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *(const f32x4*)(lse_s + qb * 32 + 8 * g + 4 * hl);
+          f32x4 p4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float p = exp2_hw(__builtin_fmaf(x[qb][r], a.scale_log2, -l4[e]));
-              if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
-              p4[e] = p;
-              pf[qb][r >> 3][r & 7] = (bf16)p;
-            }
-            pbuf[kblk][qb][g][lane] = p4;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = exp2_hw(__builtin_fmaf(x[qb][r], a.scale_log2, -l4[e]));
+            if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
+            p4[e] = p;
+            pf[qb][r >> 3][r & 7] = (bf16)p;
           }
+          pbuf[kblk][qb][g][lane] = p4;
+        }
+      };
+      auto need_mask_of = [&](int qb) {
+        return (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > t.cpos0 + qb * 32);
+      };
+      if (pwave && act[0] && act[1] && !need_mask_of(0)) {
+        // common case, straight-line: block 1's score MFMAs interleaved with block 0's
+        // softmax so that the wave's vector work runs under its own matrix work
+        contract(0);
+        __builtin_amdgcn_sched_barrier(0);
+        contract(1);
+        softmax(0, false);
+        for (int j = 0; j < KK; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // five VALU / transcendental
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        softmax(1, false);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          if (act[qb]) contract(qb);
+        if (pwave) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (act[qb]) softmax(qb, need_mask_of(qb));
         }
       }
       // P of this tile is in LDS; the prefetch of the next tile stays in flight
