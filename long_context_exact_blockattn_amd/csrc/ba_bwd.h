@@ -220,30 +220,61 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
           lim = cl < lim ? cl : lim;
         }
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
+      f32x16 s[2], dp[2];
+      bf16x8 dsf[2][2];
+      auto scores = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          s = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + n_off[kk]), qf[kk], kk == 0 ? f32x16{} : s);
-          dp = mfma32(*(const bf16x8*)(Vs + kb * 32 * D + n_off[kk]), df[kk], kk == 0 ? f32x16{} : dp);
+          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * D + n_off[kk]), qf[kk], kk == 0 ? f32x16{} : s[kb]);
+          dp[kb] = mfma32(*(const bf16x8*)(Vs + kb * 32 * D + n_off[kk]), df[kk], kk == 0 ? f32x16{} : dp[kb]);
         }
-        bf16x8 dsf[2];
+      };
+      auto make_ds = [&](int kb, bool masked) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float p = exp2_hw(__builtin_fmaf(s[r], a.scale_log2, -lse2));
-          if (need_mask) p = key <= lim ? p : 0.f;
-          dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dlt));
+          float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2));
+          if (masked) p = key <= lim ? p : 0.f;
+          dsf[kb][r >> 3][r & 7] = (bf16)(p * (dp[kb][r] - dlt));
         }
-        // dQ^T += K^T dS^T: K^T operand read transposed from the [key][d] tile
+      };
+      // dQ^T += K^T dS^T: K^T operand read transposed from the [key][d] tile
+      auto accumulate = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             const bf16* base = Ks + (kb * 32 + 16 * c2) * D;
-            dqacc[db] = mfma32(tr_pair(base, t_off[db][0], t_off[db][1]), dsf[c2], dqacc[db]);
+            dqacc[db] = mfma32(tr_pair(base, t_off[db][0], t_off[db][1]), dsf[kb][c2], dqacc[db]);
           }
+      };
+      if (!need_mask) {
+        // common case, straight-line: each 32-key block's vector work runs between the
+        // MFMAs of the next step (block 1's scores, then block 0's dQ)
+        scores(0);
+        __builtin_amdgcn_sched_barrier(0);
+        scores(1);
+        make_ds(0, false);
+        for (int j = 0; j < 2 * KK; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        accumulate(0);
+        make_ds(1, false);
+        for (int j = 0; j < 2 * DB; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x402, 8, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        accumulate(1);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          scores(kb);
+          make_ds(kb, true);
+          accumulate(kb);
+        }
       }
     };
 
