@@ -326,12 +326,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 // Eight waves: each 32-key block of the item is owned by a PAIR of waves that
 // share a SIMD.  The P wave holds K and computes S, P = exp(S - LSE) and
 // dV += P^T dO; the dS wave holds V and computes dP = dO V^T, dS = P (dP -
-// delta) and dK += dS^T Q, taking P from the P wave through LDS (fp32, in the
-// accumulator layout both waves share: lane = key, register = query).  A tile
-// of 64 query rows runs in two phases separated by a barrier: scores / dP
-// MFMAs and the P softmax, then the two gradient contractions.  Each wave
-// keeps one stationary operand and one accumulator set, so two waves fit on
-// a SIMD and each one's VALU work runs under the other's MFMAs.
+// delta) and dK += dS^T Q, taking P from the P wave through LDS (bf16, in the
+// accumulator layout both waves share: lane = key, register = query).  Each
+// tile of 64 query rows has two phases per wave: the score / dP MFMAs (with
+// the softmax on the P wave), then the two gradient contractions.  The phases
+// are skewed by one tile: between two barriers every wave runs phase 2 of
+// tile j - 1 and then phase 1 of tile j, so the dS wave's second phase (the
+// heavier one: dS on the vector ALU, then dK) overlaps the P wave's first
+// phase (the softmax) instead of following it.  One barrier per tile; three
+// tile buffers (tile j + 1 loads while tiles j - 1 and j are read) and two P
+// buffers.  Each wave keeps one stationary operand and one accumulator set,
+// so two waves fit on a SIMD and each one's VALU work runs under the other's
+// MFMAs.
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -340,12 +346,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DB = D / 32;
   constexpr int TILE = BM * D;
   constexpr int NKB = BN / 32;  // key blocks = wave pairs
-  // two buffers, each a Q tile followed by a dO tile (swizzled); separate arrays
-  // so prefetches into one buffer do not make the compiler wait before reading
-  // the other
-  __shared__ __attribute__((aligned(16))) bf16 sT0[2 * TILE], sT1[2 * TILE];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse*log2e, delta][row]
-  __shared__ __attribute__((aligned(16))) f32x4 pbuf[NKB][2][4][64];  // [key block][qb][quarter][lane]
+  // three buffers, each a Q tile followed by a dO tile (swizzled); separate
+  // arrays so prefetches into one buffer do not make the compiler wait before
+  // reading the others
+  __shared__ __attribute__((aligned(16))) bf16 sT0[2 * TILE], sT1[2 * TILE], sT2[2 * TILE];
+  __shared__ __attribute__((aligned(16))) float stat[3][2][BM];  // [buffer][lse*log2e, delta][row]
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NKB][2][2][64];  // [parity][key block][qb][half][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -413,11 +419,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
     Pos pos_load{h0, it.qt_begin}, pos_comp{h0, it.qt_begin};
-    // stage tile i: LSE and delta by ordinary loads (issued first, consumed only
-    // after the tile in flight has been processed), Q and dO by direct loads
+    // stage a tile: LSE and delta by ordinary loads (issued first, written to LDS
+    // only after the interval's compute), Q and dO by direct loads
     float st_l = INFINITY, st_d = 0.f;
     bool st_ok = false;
-    auto issue = [&](bf16* qd, bf16* dd) {
+    auto issue = [&](bf16* qd) {
       const int hh = pos_load.head;
       const QTile t = make_qtile(sc, pos_load.qtile);
       advance(pos_load);
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const int64_t base = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
       ld.issue(a.q + base, qs_s, (int)t.rows, qd, wave);
-      ld.issue(a.dout + base, qs_s, (int)t.rows, dd, wave);
+      ld.issue(a.dout + base, qs_s, (int)t.rows, qd + TILE, wave);
     };
     auto put_stats = [&](int buf) {
       if (tid < BM) {
@@ -438,17 +444,21 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    // QDs: one buffer, the Q tile followed by the dO tile
-    auto tile_step = [&](const bf16* QDs, const float* lse_s, const float* del_s) {
+    // state of the tile between its two phases: which query blocks the mask
+    // leaves active and S (P wave) or dP (dS wave)
+    bool act[2] = {false, false};
+    f32x16 x[2];
+
+    // ---- phase 1: S^T = K Q^T (P wave) or dP^T = V dO^T (dS wave), 32 queries per
+    // block (fragments read one pair of k-steps ahead of the MFMAs that use them);
+    // the P wave then forms P and hands it to the dS wave through pbuf[par]
+    auto phase1 = [&](const bf16* QDs, int sbuf, int par) __attribute__((always_inline)) {
       const QTile t = make_qtile(sc, pos_comp.qtile);
       advance(pos_comp);
-      bool act[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) act[qb] = !(a.causal && wave_kmin > t.cpos0 + qb * 32 + 31);
-      // ---- phase 1: S^T = K Q^T (P wave) or dP^T = V dO^T (dS wave), 32 queries per block
-      // (fragments read one pair of k-steps ahead of the MFMAs that use them)
+      const float* lse_s = stat[sbuf][0];
       const bf16* Xs = QDs + (pwave ? 0 : TILE);
-      f32x16 x[2];
       auto contract = [&](int qb) __attribute__((always_inline)) {
         bf16x8 fr[2][2];
         auto rd = [&](int kk2, int set) __attribute__((always_inline)) {
@@ -463,10 +473,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           x[qb] = mfma32(fr[kk2 & 1][1], sf[2 * kk2 + 1], x[qb]);
         }
       };
-      // P = exp(S - LSE) of block qb (zero where masked), to LDS for the dS wave and
-      // as bf16 operands for dV
-      bf16x8 pf[2][2];
+      // P = exp(S - LSE) of block qb (zero where masked), in bf16 to LDS for both
+      // waves' second phase
       auto softmax = [&](int qb, bool need_mask) __attribute__((always_inline)) {
+        bf16x8 pf[2];
         const int64_t qc0 = t.cpos0 + qb * 32;
         // allowed iff key_ok and (not causal or query coordinate >= key coordinate)
         int qmin = -1;  // smallest allowed query index inside the block, relative to qc0
@@ -482,17 +492,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 l4 = *(const f32x4*)(lse_s + qb * 32 + 8 * g + 4 * hl);
-          f32x4 p4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             float p = exp2_hw(__builtin_fmaf(x[qb][r], a.scale_log2, -l4[e]));
             if (need_mask) p = (8 * g + 4 * hl + e) >= qmin ? p : 0.f;
-            p4[e] = p;
-            pf[qb][r >> 3][r & 7] = (bf16)p;
+            pf[r >> 3][r & 7] = (bf16)p;
           }
-          pbuf[kblk][qb][g][lane] = p4;
         }
+        pbuf[par][kblk][qb][0][lane] = pf[0];
+        pbuf[par][kblk][qb][1][lane] = pf[1];
       };
       auto need_mask_of = [&](int qb) {
         return (t.rows < BM) || (it.krows < BN) || (a.causal && wave_kmax > t.cpos0 + qb * 32);
@@ -520,27 +529,32 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             if (act[qb]) softmax(qb, need_mask_of(qb));
         }
       }
-      // P of this tile is in LDS; the prefetch of the next tile stays in flight
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // ---- phase 2: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
-      // transposed operand is read from the [query][d] tile
+    };
+
+    // ---- phase 2: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
+    // transposed operand is read from the [query][d] tile
+    auto phase2 = [&](const bf16* QDs, int sbuf, int par) __attribute__((always_inline)) {
+      const float* del_s = stat[sbuf][1];
       const bf16* Ys = QDs + (pwave ? TILE : 0);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (!act[qb]) continue;
         bf16x8 yf[2];
         if (pwave) {
-          yf[0] = pf[qb][0];
-          yf[1] = pf[qb][1];
+          // its own P, back from LDS: no registers held across the barrier
+          yf[0] = pbuf[par][kblk][qb][0][lane];
+          yf[1] = pbuf[par][kblk][qb][1][lane];
         } else {
+          const bf16x8 p0 = pbuf[par][kblk][qb][0][lane];
+          const bf16x8 p1 = pbuf[par][kblk][qb][1][lane];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const f32x4 p4 = pbuf[kblk][qb][g][lane];
             const f32x4 d4 = *(const f32x4*)(del_s + qb * 32 + 8 * g + 4 * hl);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
-              yf[r >> 3][r & 7] = (bf16)(p4[e] * (x[qb][r] - d4[e]));
+              const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
+              yf[r >> 3][r & 7] = (bf16)(p * (x[qb][r] - d4[e]));
             }
           }
         }
@@ -561,22 +575,33 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    issue(sT0, sT0 + TILE);
+    // interval j (0 <= j <= n_iter): load tile j + 1 into Tl, phase 2 of tile
+    // j - 1 (buffer Tp), phase 1 of tile j (buffer Tc); buffer and statistics
+    // slots rotate with j mod 3, P slots with j mod 2
+    auto interval = [&](bf16* Tc, const bf16* Tp, bf16* Tl, int64_t j, int rot) __attribute__((always_inline)) {
+      const int par = (int)(j & 1);
+      if (j + 1 < n_iter) issue(Tl);
+      if (j >= 1) phase2(Tp, rot == 0 ? 2 : rot - 1, par ^ 1);
+      // x and pf are rewritten by phase 1: keep the two phases apart
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < n_iter) phase1(Tc, rot, par);
+      if (j + 1 < n_iter) put_stats(rot == 2 ? 0 : rot + 1);
+      wait_vmem();
+      __syncthreads();
+    };
+
+    issue(sT0);
     put_stats(0);
     wait_vmem();
     __syncthreads();
-    for (int64_t i = 0; i < n_iter; i += 2) {
-      if (i + 1 < n_iter) issue(sT1, sT1 + TILE);
-      tile_step(sT0, stat[0][0], stat[0][1]);
-      if (i + 1 < n_iter) put_stats(1);
-      wait_vmem();
-      __syncthreads();
-      if (i + 1 >= n_iter) break;
-      if (i + 2 < n_iter) issue(sT0, sT0 + TILE);
-      tile_step(sT1, stat[1][0], stat[1][1]);
-      if (i + 2 < n_iter) put_stats(0);
-      wait_vmem();
-      __syncthreads();
+    // unrolled by three so that every buffer sits at a fixed LDS address
+    for (int64_t j = 0;; j += 3) {
+      interval(sT0, sT2, sT1, j, 0);
+      if (j + 1 > n_iter) break;
+      interval(sT1, sT0, sT2, j + 1, 1);
+      if (j + 2 > n_iter) break;
+      interval(sT2, sT1, sT0, j + 2, 2);
+      if (j + 3 > n_iter) break;
     }
   }
 
