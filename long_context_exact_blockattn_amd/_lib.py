@@ -117,6 +117,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _require(ref, specs):
+    """Every tensor of specs [(tensor or None, name, dtype name or None)] must live on ref's GPU
+    and have the named dtype: the kernels take raw device pointers and size every access from
+    the descriptor, so a host tensor or a narrower dtype would be read or written out of bounds."""
+    import torch
+    if not ref.is_cuda:
+        raise ValueError("tensors must be on a GPU (got a host tensor)")
+    for t, name, dt in specs:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device} (got {t.device})")
+        if dt is not None and t.dtype != getattr(torch, dt):
+            raise ValueError(f"{name} must be {dt} (got {t.dtype})")
+
+
 def _stream(stream):
     """A hipStream_t from None (torch's current stream), a torch stream, or a raw handle."""
     if stream is not None:
@@ -177,6 +193,8 @@ def _dtype_code(t, name):
 def blockattn_fwd(q, k, v, o, lse, *, mode=BA_OVERWRITE, o_final=None, q_pos0=0, k_pos0=0,
                   causal=True, scale=None, stream=None):
     """One ring step; see blockattn_fwd in include/blockattn.h."""
+    _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
+                 (lse, "lse", "float32"), (o_final, "o_final", "bfloat16")])
     desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
     if tuple(v.shape) != tuple(k.shape) or _bshd_strides(v, "v") != _bshd_strides(k, "k"):
         raise ValueError("v must match k in shape and strides")
@@ -190,6 +208,8 @@ def blockattn_fwd(q, k, v, o, lse, *, mode=BA_OVERWRITE, o_final=None, q_pos0=0,
 
 def lse_merge(o_acc, lse_acc, o_part, lse_part, *, o_final=None, stream=None):
     """(o_acc, lse_acc) := merge with (o_part, lse_part); see lse_merge in include/blockattn.h."""
+    _require(o_acc, [(o_acc, "o_acc", "float32"), (lse_acc, "lse_acc", "float32"), (o_part, "o_part", None),
+                     (lse_part, "lse_part", "float32"), (o_final, "o_final", "bfloat16")])
     desc = make_desc(o_acc, None)
     _same_layout(o_acc, o_part, "o_part")
     _same_layout(o_acc, o_final, "o_final")
@@ -202,7 +222,11 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, *, o_final=None, stream=None):
 
 
 def s2attn_fwd(q, k, v, o, lse, *, group, shift_head0, scale=None, stream=None):
+    _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
+                 (lse, "lse", "float32")])
     desc = make_desc(q, k, causal=True, scale=scale)
+    if tuple(v.shape) != tuple(k.shape) or _bshd_strides(v, "v") != _bshd_strides(k, "k"):
+        raise ValueError("v must match k in shape and strides")
     _same_layout(q, o, "o")
     _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
     s2 = BaS2Desc(int(group), int(shift_head0))
@@ -211,10 +235,11 @@ def s2attn_fwd(q, k, v, o, lse, *, group, shift_head0, scale=None, stream=None):
     _check(st, "s2attn_fwd")
 
 
-def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None, flags=0,
-                  q_pos0=0, k_pos0=0, causal=True, scale=None, stream=None):
-    """One ring step of the backward; see blockattn_bwd in include/blockattn.h."""
-    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+def _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final):
+    _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", "bfloat16"),
+                 (dout, "dout", "bfloat16"), (lse, "lse", "float32"), (delta, "delta", "float32"),
+                 (dq_acc, "dq_acc", "float32"), (dk, "dk", None), (dv, "dv", None),
+                 (dq_final, "dq_final", "bfloat16")])
     for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
         _same_layout(q, t, n)
     for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
@@ -225,6 +250,13 @@ def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None
     shape = (q.shape[0], q.shape[2], q.shape[1])
     _stats_ok(lse, shape, "lse")
     _stats_ok(delta, shape, "delta")
+
+
+def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None, flags=0,
+                  q_pos0=0, k_pos0=0, causal=True, scale=None, stream=None):
+    """One ring step of the backward; see blockattn_bwd in include/blockattn.h."""
+    _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final)
+    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
     st = load().blockattn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                               _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
                               _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
@@ -233,12 +265,8 @@ def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None
 
 def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_head0, dq_final=None,
                flags=0, scale=None, stream=None):
+    _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final)
     desc = make_desc(q, k, causal=True, scale=scale)
-    for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
-        _same_layout(q, t, n)
-    shape = (q.shape[0], q.shape[2], q.shape[1])
-    _stats_ok(lse, shape, "lse")
-    _stats_ok(delta, shape, "delta")
     s2 = BaS2Desc(int(group), int(shift_head0))
     st = load().s2attn_bwd(ctypes.byref(desc), ctypes.byref(s2), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
@@ -248,6 +276,8 @@ def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_hea
 
 def _dense_bf16(t, name, fn):
     import torch
+    if not t.is_cuda:
+        raise ValueError(f"{fn}: {name} must be on a GPU (got a host tensor)")
     if t.dtype != torch.bfloat16:
         raise BlockAttnError(BA_ERR_UNSUPPORTED, f"{fn} ({name} must be bf16)")
     if not t.is_contiguous():

@@ -198,6 +198,7 @@ int ulysses_launch(bool pack, const void* src, void* dst, int64_t batch, int64_t
   a.N = n_devices;
   a.n_chunks = n_chunks;
   const int64_t blocks = (n_chunks + 255) / 256;
+  if (blocks > 0x7fffffffLL) return BA_ERR_SHAPE;
   if (pack)
     hipLaunchKernelGGL(ulysses_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else
@@ -218,6 +219,7 @@ int gemm_launch(int epi, const void* a, const void* b, const void* b3, void* c, 
   g.tiles_m = (int32_t)((m + kGemmBM - 1) / kGemmBM);
   g.tiles_n = n_out / (epi == EPI_SWIGLU ? 128 : 256);
   g.n_items = (int64_t)g.tiles_m * g.tiles_n;
+  if (g.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(gemm_nt_kernel<EPI_SWIGLU>, dim3((unsigned)g.n_items), dim3(kGemmThreads), 0, stream, g);
   else

@@ -190,3 +190,44 @@ def test_bpt_ffn_validation(lib):
     assert lib.bpt_ffn(None, *args[1:], 100, 256, 256, 64, None) == _lib.BA_ERR_NULL
     assert lib.bpt_ffn(P(FAKE + 2), *args[1:], 100, 256, 256, 64, None) == _lib.BA_ERR_ALIGN
     assert lib.bpt_ffn(None, None, None, None, None, None, 0, 256, 256, 64, None) == _lib.BA_OK
+
+
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor in the binding's checks (no data, never passed on)."""
+
+    def __init__(self, dtype, device="cuda:0"):
+        import torch
+        self.is_cuda = True
+        self.device = torch.device(device)
+        self.dtype = dtype
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    import torch
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.blockattn_fwd(q, q, q, q.float(), lse)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.lse_merge(q.float(), lse, q.float(), lse)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.blockattn_bwd(q, q, q, q, q, lse, lse, q.float(), q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.s2attn_fwd(q, q, q, q.float(), lse, group=64, shift_head0=2)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.ulysses_pack(q, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.bpt_ffn(q[0, :, 0], q[0, :, 0], q[0, :, 0], q[0, :, 0])
+
+
+def test_binding_dtype_and_device_requirements():
+    import torch
+    q = _FakeGpuTensor(torch.bfloat16)
+    _lib._require(q, [(q, "q", "bfloat16"), (_FakeGpuTensor(torch.float32), "lse", "float32"), (None, "x", "float32")])
+    # a bf16 statistics tensor would be written with fp32 stores past its end
+    with pytest.raises(ValueError, match="lse must be float32"):
+        _lib._require(q, [(_FakeGpuTensor(torch.bfloat16), "lse", "float32")])
+    with pytest.raises(ValueError, match="k must be bfloat16"):
+        _lib._require(q, [(_FakeGpuTensor(torch.float32), "k", "bfloat16")])
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        _lib._require(q, [(_FakeGpuTensor(torch.bfloat16, "cuda:1"), "v", "bfloat16")])
