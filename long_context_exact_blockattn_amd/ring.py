@@ -109,7 +109,9 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
                            o_final=out if t == len(order) - 1 else None,
                            k_pos0=c0, causal=causal, scale=scale, stream=main)
         computed[slot].record(main)
-    for t in kbuf + vbuf:
+    # the side stream read k and v and wrote the staging buffers: none of them may be
+    # reused by the allocator before that stream's work is done
+    for t in kbuf + vbuf + [k, v]:
         t.record_stream(side)
     return out, lse, o_acc
 
@@ -124,6 +126,8 @@ def ring_backward(q, k, v, o, dout, lse, n_chunks, order=None, *, causal=True, s
     """
     bounds = _bounds(k.shape[1], n_chunks)
     order = list(range(len(bounds))) if order is None else list(order)
+    if sorted(order) != list(range(len(bounds))):
+        raise ValueError("order must be a permutation of the chunk indices")
     b, s, hq, d = q.shape
     delta = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
     dq_acc = torch.zeros(b, s, hq, d, device=q.device, dtype=torch.float32)

@@ -231,3 +231,15 @@ def test_binding_dtype_and_device_requirements():
         _lib._require(q, [(_FakeGpuTensor(torch.float32), "k", "bfloat16")])
     with pytest.raises(ValueError, match="must be on cuda:0"):
         _lib._require(q, [(_FakeGpuTensor(torch.bfloat16, "cuda:1"), "v", "bfloat16")])
+
+
+def test_ring_drivers_reject_bad_chunk_orders():
+    import torch
+    from long_context_exact_blockattn_amd import ring_backward, ring_forward
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 64)
+    for bad in ([0, 0, 1, 2], [0, 1, 2], [1, 2, 3, 4]):
+        with pytest.raises(ValueError, match="permutation"):
+            ring_forward(q, q, q, 4, bad)
+        with pytest.raises(ValueError, match="permutation"):
+            ring_backward(q, q, q, q, q, lse, 4, bad)
