@@ -254,3 +254,18 @@ def test_ring_forward_staged_equals_ring_forward(n_chunks, S, B):
     o_ref, lse_ref = attention_forward(f64(q), f64(k), f64(v))
     log(f"staged ring n={n_chunks} S={S} B={B}: max |O - O_ref| {max_err(got[0], o_ref):.3e}")
     assert max_err(got[2], o_ref) <= TOL_O and max_err(got[1], lse_ref) <= TOL_LSE
+
+
+def test_binding_rejects_wrong_dtype_or_host_tensor_on_gpu():
+    # validation only: every call below raises before a pointer reaches the library
+    q, k, v = _to_dev(*make_inputs(1, 128, 2, 2, 128, seed=5))
+    o = torch.empty(1, 128, 2, 128, device=dev())
+    lse = torch.empty(1, 2, 128, device=dev())
+    with pytest.raises(ValueError, match="lse must be float32"):
+        ba.blockattn_fwd(q, k, v, o, lse.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="k must be bfloat16"):
+        ba.blockattn_fwd(q, k.float(), v, o, lse)
+    with pytest.raises(ValueError, match="must be on"):
+        ba.blockattn_fwd(q, k.cpu(), v, o, lse)
+    with pytest.raises(ValueError, match="dq_acc must be float32"):
+        ba.blockattn_bwd(q, k, v, q, q, lse, lse, q, k, v)
