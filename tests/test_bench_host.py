@@ -1,0 +1,93 @@
+"""Host-side tests of bench.py: the one-GPU refusal and the profile summaries it reports from.
+
+The summaries read rocprofv3 result databases (sqlite); these tests build tiny databases with the
+same tables, so the arithmetic behind the committed profiles (per-kernel averages, the copy
+calibration of the byte counters, the source check of the traffic record) is checked without a GPU.
+"""
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _kernels_db(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    con = sqlite3.connect(path)
+    con.execute("create table kernels (name text, duration integer, grid_x integer, workgroup_x integer, "
+                "vgpr_count integer, accum_vgpr_count integer, scratch_size integer, lds_size integer)")
+    con.executemany("insert into kernels values (?, ?, ?, ?, ?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_trace_summary_averages_per_kernel(tmp_path, capsys):
+    a = ("void ba::fwd_kernel<128>(ba::FwdArgs)", 256, 256, 128, 0, 16, 65536)
+    b = ("merge", 1024, 256, 12, 0, 0, 0)
+    _kernels_db(str(tmp_path / "run" / "x_results.db"),
+                [(a[0], 1000, *a[1:]), (a[0], 2000, *a[1:]), (b[0], 500, *b[1:])])
+    _kernels_db(str(tmp_path / "run2" / "y_results.db"), [(a[0], 3000, *a[1:])])
+    bench.trace_summary(str(tmp_path))
+    lines = capsys.readouterr().out.strip().splitlines()
+    assert len(lines) == 2
+    # sorted by total time; durations are nanoseconds, the summary prints microseconds
+    assert lines[0].split()[:5] == ["3", "calls", "avg", "2.000", "us"] and "fwd_kernel<128>" in lines[0]
+    assert "lds 65536" in lines[0] and "scratch 16" in lines[0]
+    assert lines[1].split()[:4] == ["1", "calls", "avg", "0.500"]
+
+
+def _counters_db(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (dispatch_id integer, kernel_name text, counter_name text, "
+                "value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    k = "ba::fwd_kernel<128>(ba::FwdArgs)"
+    # two dispatches; each counter arrives split over several rows (per XCD), summed per dispatch
+    _counters_db(str(tmp_path / "f" / "a_results.db"),
+                 [(1, k, "FETCH_SIZE", 60.0), (1, k, "FETCH_SIZE", 40.0), (2, k, "FETCH_SIZE", 300.0),
+                  (3, "other", "FETCH_SIZE", 1e9)])
+    _counters_db(str(tmp_path / "w" / "a_results.db"), [(1, k, "WRITE_SIZE", 50.0), (2, k, "WRITE_SIZE", 50.0)])
+    # the 1 GiB copy: the fetch counter reports half the bytes, the write counter all of them
+    _counters_db(str(tmp_path / "cf" / "a_results.db"), [(1, "copy", "FETCH_SIZE", 524288.0), (2, "fill", "FETCH_SIZE", 8.0)])
+    _counters_db(str(tmp_path / "cw" / "a_results.db"), [(1, "copy", "WRITE_SIZE", 1048576.0)])
+    out = str(tmp_path / "traffic.json")
+    bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"), out)
+    rec = json.load(open(out))
+    assert rec["copy_calibration"]["fetch_scale"] == 2.0 and rec["copy_calibration"]["write_scale"] == 1.0
+    assert rec["fetch_size_kib_per_dispatch"] == [100.0, 300.0]
+    assert rec["hbm_fetch_bytes_per_launch"] == 200 * 1024 * 2
+    assert rec["hbm_write_bytes_per_launch"] == 50 * 1024
+    assert rec["hbm_bytes_per_launch"] == 200 * 1024 * 2 + 50 * 1024
+    # the bench line reports the record only while the kernel source is the one it was taken on
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    os.replace(out, str(tmp_path / "fwd_kernel_d128_traffic.json"))
+    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC) == rec["hbm_bytes_per_launch"]
+    rec["kernel_source_sha"] = "0" * 16
+    json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_traffic.json"), "w"))
+    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC) is None
+    assert bench._traffic("no_such_kernel", bench.FWD_SRC) is None
+
+
+def test_missing_profile_directory_is_reported(tmp_path):
+    with pytest.raises(SystemExit, match="no rocprofv3"):
+        bench.trace_summary(str(tmp_path))
