@@ -42,13 +42,12 @@ struct FwdArgs {
   int64_t n_items;
 };
 
-// Query blocks of 32 rows per wave: with two, every K or V fragment read from
-// LDS feeds two MFMAs (LDS read bandwidth caps a one-block design), at one
-// wave per SIMD.
-#ifndef BA_FWD_QB
-#define BA_FWD_QB 1
-#endif
-constexpr int kFwdQB = BA_FWD_QB;
+// One 32-row query block per wave, two waves per SIMD.  The loops below are
+// written over kFwdQB blocks per wave: with two, every K or V fragment read
+// from LDS would feed two MFMAs (half the LDS bytes per MFMA), but the ~380
+// live registers that takes leave one wave per SIMD, which measures about half
+// as fast.
+constexpr int kFwdQB = 1;
 constexpr int kFwdThreads = 256;
 constexpr int kFwdBM = (kFwdThreads / 64) * 32 * kFwdQB;
 constexpr int kFwdBN = 64;
