@@ -36,14 +36,17 @@ def _src_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel_key, src_path):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
+def _traffic(kernel_key, src_path, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this
+    workload and the kernel source has not changed since."""
     path = os.path.join(PROFILE_DIR, f"{kernel_key}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != _src_sha(src_path):
+        return None
+    if rec.get("workload", "").split(" ")[0] != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -584,7 +587,7 @@ def main():
     achieved = flop / r["launches_per_step"] / (avg_launch_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic("fwd_kernel_d128", r["src"]) if w.head_dim == 128 else None,
+                "traffic": _traffic("fwd_kernel_d128", r["src"], w.name),
                 "kernel": r["kernel"], "avg_launch_ms": round(avg_launch_ms, 4),
                 "launches_per_step": r["launches_per_step"]}
     line = {

@@ -81,11 +81,15 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # the bench line reports the record only while the kernel source is the one it was taken on
     monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
     os.replace(out, str(tmp_path / "fwd_kernel_d128_traffic.json"))
-    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC) == rec["hbm_bytes_per_launch"]
+    wl = "llama2_7b_s32k_ring8"
+    assert rec["workload"].split(" ")[0] == wl
+    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC, wl) == rec["hbm_bytes_per_launch"]
+    # ... and only on the workload it was taken on
+    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC, "gqa_llama3_8b_s128k_ring16") is None
     rec["kernel_source_sha"] = "0" * 16
     json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_traffic.json"), "w"))
-    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC) is None
-    assert bench._traffic("no_such_kernel", bench.FWD_SRC) is None
+    assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC, wl) is None
+    assert bench._traffic("no_such_kernel", bench.FWD_SRC, wl) is None
 
 
 def test_missing_profile_directory_is_reported(tmp_path):
