@@ -213,7 +213,6 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
       }
       // ---- online softmax (base 2), per query block
       bf16x8 pf[QB][4];
-      float alpha[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float mx = -INFINITY;
@@ -228,7 +227,7 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
         const float mx2 = mx * a.scale_log2;
         const float m_new = (mx2 > m_run[qb] + 8.f) ? mx2 : m_run[qb];
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha[qb] = exp2_hw(m_run[qb] - m_use);
+        const float m_old = m_run[qb];
         float rsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -238,12 +237,18 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
             rsum += p;
             pf[qb][kb * 2 + (r >> 3)][r & 7] = (bf16)p;
           }
-        l_run[qb] = l_run[qb] * alpha[qb] + rsum;
-        m_run[qb] = m_new;
-        if (__any(alpha[qb] != 1.f)) {
+        // alpha = 2^(m_old - m_use) differs from 1 only where the running max moved
+        // (or where it was -inf, with O and l still 0): the rescale is decided on
+        // the max alone and the exponential stays off the common path
+        if (__any(m_new != m_old)) {
+          const float al = exp2_hw(m_old - m_use);
+          l_run[qb] = l_run[qb] * al + rsum;
 #pragma unroll
-          for (int i = 0; i < DB; ++i) oacc[qb][i] *= alpha[qb];
+          for (int i = 0; i < DB; ++i) oacc[qb][i] *= al;
+        } else {
+          l_run[qb] = l_run[qb] + rsum;
         }
+        m_run[qb] = m_new;
       }
       // ---- O^T += V^T P^T ; V^T operand read transposed from the [key][d] tile,
       // each fragment feeding QB MFMAs
