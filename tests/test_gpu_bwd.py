@@ -164,3 +164,36 @@ def test_backward_full_size_one_head_and_sampled_rows():
     rel = float(((lhs - rhs).abs() / norm).max())
     log(f"<dV,V> vs <dO,O> on every head: max |diff| / sum_i |dO_i.O_i| = {rel:.3e}")
     assert rel <= 1e-2
+
+
+def test_packed_qkv_strided_views_forward_and_backward():
+    # q, k, v and every output as slices of packed [B, S, 3, H, D] buffers: (b, s, h) strides
+    # (3SHD, 3HD, D) instead of dense ones, through the same entry points
+    B, S, H, D = 2, 333, 4, 128
+    q, k, v, do = make_inputs(B, S, H, H, D, seed=44, with_dout=True)
+    packed = torch.stack([q, k, v], dim=2).to(dev())
+    qv, kv, vv = packed[:, :, 0], packed[:, :, 1], packed[:, :, 2]
+    assert qv.stride()[:3] == (S * 3 * H * D, 3 * H * D, D) and not qv.is_contiguous()
+    f32 = torch.zeros(B, S, 3, H, D, device=dev())
+    b16 = torch.zeros(B, S, 3, H, D, device=dev(), dtype=torch.bfloat16)
+    o_acc, dq_acc = f32[:, :, 0], f32[:, :, 1]
+    out, dov, dq = b16[:, :, 0], b16[:, :, 1], b16[:, :, 2]
+    dov.copy_(do.to(dev()))
+    gk = torch.zeros(B, S, 3, H, D, device=dev(), dtype=torch.bfloat16)
+    dk, dv = gk[:, :, 0], gk[:, :, 1]
+    lse = torch.empty(B, H, S, device=dev())
+    delta = torch.empty(B, H, S, device=dev())
+    ba.blockattn_fwd(qv, kv, vv, o_acc, lse, o_final=out)
+    ba.blockattn_bwd(qv, kv, vv, out, dov, lse, delta, dq_acc, dk, dv, dq_final=dq,
+                     flags=ba.BA_BWD_COMPUTE_DELTA | ba.BA_BWD_FINALIZE_DQ)
+    torch.cuda.synchronize()
+    from oracle import attention_forward
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    eo = float(np.abs(f64(o_acc) - o_ref).max())
+    el = float(np.abs(f64(lse) - l_ref).max())
+    log(f"packed-QKV strided views fwd: max|O-ref| {eo:.3e} max|LSE-ref| {el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do))[:3]
+    _check_grads("packed-QKV strided views bwd", (dq, dk, dv), ref)
+    # the slices the calls must not touch are still zero
+    assert not f32[:, :, 2].any() and not gk[:, :, 2].any()
