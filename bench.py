@@ -277,7 +277,7 @@ def run_training(w, steps, warmup):
 
 def cpu_baseline(w, budget_heads=2):
     """The oracle as it stands, on the first query heads of the same workload (all ring steps):
-    about 12 s of host work at the 32K headline shape."""
+    about 12 s of host work at the 32K headline shape; short sequences are timed in full."""
     import numpy as np
 
     from oracle import ring_attention_forward
@@ -289,7 +289,7 @@ def cpu_baseline(w, budget_heads=2):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
-    heads = list(range(budget_heads))
+    heads = list(range(w.heads_q if w.seqlen <= 4096 else min(budget_heads, w.heads_q)))
     kv_heads = sorted({h // (w.heads_q // w.heads_kv) for h in heads})
     qn = q[:, :, heads].float().numpy().astype(np.float64)
     kn = k[:, :, kv_heads].float().numpy().astype(np.float64)
