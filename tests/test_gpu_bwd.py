@@ -98,16 +98,17 @@ def test_delta_kernel():
     assert err <= 1e-4
 
 
-@pytest.mark.parametrize("Hq,Hkv,shift_head0", [(4, 4, 2), (8, 2, 4)])
-def test_s2_backward(Hq, Hkv, shift_head0):
-    S, G, D = 2048, 512, 128
-    q, k, v, do = make_inputs(1, S, Hq, Hkv, D, seed=97, with_dout=True)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,shift_head0", [(1, 4, 4, 2), (1, 8, 2, 4), (2, 4, 2, 2)])
+def test_s2_backward(B, Hq, Hkv, shift_head0, D):
+    S, G = 2048, 512
+    q, k, v, do = make_inputs(B, S, Hq, Hkv, D, seed=97 + D, with_dout=True)
     qd, kd, vd, dod = _to_dev(q, k, v, do)
     o, lse = ba.s2_forward(qd, kd, vd, G, shift_head0)
     got = ba.s2_backward(qd, kd, vd, o, dod, lse, G, shift_head0)
     torch.cuda.synchronize()
     ref = attention_backward(f64(q), f64(k), f64(v), f64(do), s2=S2Spec(G, shift_head0, S))[:3]
-    _check_grads(f"s2 bwd Hq{Hq} Hkv{Hkv} shift_head0={shift_head0}", got, ref)
+    _check_grads(f"s2 bwd B{B} Hq{Hq} Hkv{Hkv} D{D} shift_head0={shift_head0}", got, ref)
 
 
 def test_s2_backward_llama2_7b_s8k_heads_subset():

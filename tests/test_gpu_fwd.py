@@ -181,15 +181,16 @@ def test_fused_merge_equals_standalone_merge():
     assert max_err(o1, f64(o2)) <= 1e-5 and max_err(l1, f64(l2)) <= 1e-5
 
 
-@pytest.mark.parametrize("Hq,Hkv,shift_head0", [(4, 4, 2), (8, 2, 4), (2, 2, 2)])
-def test_s2_forward(Hq, Hkv, shift_head0):
-    S, G, D = 2048, 512, 128
-    q, k, v = make_inputs(1, S, Hq, Hkv, D, seed=51)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,Hq,Hkv,shift_head0", [(1, 4, 4, 2), (1, 8, 2, 4), (1, 2, 2, 2), (2, 4, 2, 2)])
+def test_s2_forward(B, Hq, Hkv, shift_head0, D):
+    S, G = 2048, 512
+    q, k, v = make_inputs(B, S, Hq, Hkv, D, seed=51 + D)
     qd, kd, vd = _to_dev(q, k, v)
     o, lse = ba.s2_forward(qd, kd, vd, G, shift_head0, o_dtype=torch.float32)
     torch.cuda.synchronize()
     o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), s2=S2Spec(G, shift_head0, S))
-    _check_pair(f"s2 fwd Hq{Hq} Hkv{Hkv} shift_head0={shift_head0}", o, lse, o_ref, l_ref)
+    _check_pair(f"s2 fwd B{B} Hq{Hq} Hkv{Hkv} D{D} shift_head0={shift_head0}", o, lse, o_ref, l_ref)
 
 
 def test_s2_full_group_no_shift_equals_causal():
