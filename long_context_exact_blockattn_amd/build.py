@@ -15,6 +15,24 @@ HIPCC_FLAGS = [
 ]
 
 
+EXAMPLE_OUT = os.path.join(HERE, "abi_example")
+
+
+def build_example(verbose=False):
+    """The C-ABI example program (host code only), linked against the in-tree library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = EXAMPLE_OUT + ".tmp"
+    cmd = [hipcc, "-O2", "-std=c++17", os.path.join(CSRC, "abi_example.cpp"), "-o", tmp,
+           "-L" + HERE, "-lblockattn", "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-4000:]}")
+    os.replace(tmp, EXAMPLE_OUT)
+    return EXAMPLE_OUT
+
+
 def build_library(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
@@ -30,3 +48,4 @@ def build_library(verbose=False):
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_example(verbose=True))
