@@ -361,7 +361,21 @@ COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_VALU_
             "SQ_WAIT_ANY SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
 
 
-def counter_summary(d):
+def _counters(kernel_key, src_path, workload):
+    """MFMA-busy / VALU-busy of the committed counter summary, if it was taken on this workload and
+    the kernel source has not changed since."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_key}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != _src_sha(src_path) or rec.get("workload") != workload:
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "valu_busy_est", "valu_per_mfma", "trans_per_mfma",
+                                "lds_per_mfma", "wave_waiting")}
+
+
+def counter_summary(d, out=None):
     """MFMA-busy beside VALU-busy for the forward kernel, from one rocprofv3 --pmc pass with COUNTERS.
 
     Per dispatch: cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); MFMA busy =
@@ -393,9 +407,19 @@ def counter_summary(d):
             "mfma": c["SQ_INSTS_MFMA"],
         })
     tot = sum(r["mfma"] for r in rows)
+    keys = ("mfma_busy", "valu_busy_est", "valu_per_mfma", "trans_per_mfma", "lds_per_mfma", "wave_waiting")
+    avg = {k: sum(r[k] * r["mfma"] for r in rows) / tot for k in keys}
     print(f"{len(rows)} dispatches of fwd_kernel<128>; MFMA-weighted averages:")
-    for k in ("mfma_busy", "valu_busy_est", "valu_per_mfma", "trans_per_mfma", "lds_per_mfma", "wave_waiting"):
-        print(f"  {k:15s} {sum(r[k] * r['mfma'] for r in rows) / tot:8.3f}")
+    for k in keys:
+        print(f"  {k:15s} {avg[k]:8.3f}")
+    if out:
+        rec = {"kernel": "ba::fwd_kernel<128>", "workload": "llama2_7b_s32k_ring8",
+               "kernel_source_sha": _src_sha(FWD_SRC), "dispatches": len(rows),
+               "command": f"rocprofv3 --pmc {COUNTERS} -d {d} -o busy -- python -u bench.py --steps 1 "
+                          "--warmup 0 --no-cpu-baseline --no-side-measurements",
+               **{k: round(v, 4) for k, v in avg.items()}}
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
 
 
 def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
@@ -554,7 +578,7 @@ def main():
                     help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.counter_summary:
-        counter_summary(args.counter_summary)
+        counter_summary(args.counter_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_counters.json"))
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
@@ -588,6 +612,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic("fwd_kernel_d128", r["src"], w.name),
+                # MFMA-busy beside VALU-busy from the committed rocprofv3 --pmc summary
+                "counters": _counters("fwd_kernel_d128", r["src"], w.name),
                 "kernel": r["kernel"], "avg_launch_ms": round(avg_launch_ms, 4),
                 "launches_per_step": r["launches_per_step"]}
     line = {

@@ -95,3 +95,17 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
 def test_missing_profile_directory_is_reported(tmp_path):
     with pytest.raises(SystemExit, match="no rocprofv3"):
         bench.trace_summary(str(tmp_path))
+
+
+def test_counter_record_is_reported_only_when_current(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    rec = {"workload": "llama2_7b_s32k_ring8", "kernel_source_sha": bench._src_sha(bench.FWD_SRC),
+           "mfma_busy": 0.5, "valu_busy_est": 0.2, "valu_per_mfma": 5.0, "trans_per_mfma": 1.0,
+           "lds_per_mfma": 1.5, "wave_waiting": 0.3}
+    json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_counters.json"), "w"))
+    got = bench._counters("fwd_kernel_d128", bench.FWD_SRC, "llama2_7b_s32k_ring8")
+    assert got == {k: rec[k] for k in got} and set(got) >= {"mfma_busy", "valu_busy_est"}
+    assert bench._counters("fwd_kernel_d128", bench.FWD_SRC, "gqa_llama3_8b_s128k_ring16") is None
+    rec["kernel_source_sha"] = "f" * 16
+    json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_counters.json"), "w"))
+    assert bench._counters("fwd_kernel_d128", bench.FWD_SRC, "llama2_7b_s32k_ring8") is None
