@@ -11,12 +11,12 @@
 //
 // Online softmax (Milakov & Gimelshein's online normaliser, cited by the Ring
 // Attention summary's references): running max m and sum l per row, in base 2
-// with tau*log2(e) folded into one FMA; m is only raised when a tile's max
-// exceeds it by more than 2^8, so the O rescale is rare; a fully masked row
-// keeps m = -inf and l = 0 without producing NaN.  The epilogue turns (acc, m, l) into the
-// chunk's partial pair and, in ACCUMULATE mode, merges it into the running
-// pair (O_acc, LSE_acc) in fp32 -- the order-independent combination of the
-// Ring Attention summary (Summary).
+// with tau*log2(e) folded into one FMA; m is only raised when a tile's (base-2)
+// max exceeds it by more than 8, so the O rescale is rare; a fully masked row
+// keeps m = -inf and l = 0 without producing NaN.  The epilogue turns (acc, m,
+// l) into the chunk's partial pair and, in ACCUMULATE mode, merges it into the
+// running pair (O_acc, LSE_acc) in fp32 -- the order-independent combination of
+// the Ring Attention summary (Summary).
 #pragma once
 
 #include "ba_common.h"
@@ -222,8 +222,8 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
         mx = halves_max(mx);
         // The running max moves only when a tile's max exceeds it by more than 8
-        // (base 2): p = 2^(s - m) then stays <= 256, exact in fp32 sums and in
-        // bf16's range, and the O rescale below is skipped on almost every tile.
+        // (base 2): p = 2^(s - m) then stays <= 256, far inside the fp32 and bf16
+        // ranges, and the O rescale below is skipped on almost every tile.
         const float mx2 = mx * a.scale_log2;
         const float m_new = (mx2 > m_run[qb] + 8.f) ? mx2 : m_run[qb];
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
