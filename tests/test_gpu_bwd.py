@@ -217,3 +217,23 @@ def test_tiny_sequences_forward_and_backward(S, D):
         assert resid <= 1e-3 and ev <= TOL_GRAD
         return
     _check_grads(f"tiny S={S} D={D}", got, (dq, dk, dv))
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_explicit_softmax_scale_forward_and_backward(scale):
+    # a caller-given scale instead of 1/sqrt(D): forward pair and all three gradients
+    B, S, Hq, Hkv, D, n = 1, 640, 4, 2, 128, 3
+    q, k, v, do = make_inputs(B, S, Hq, Hkv, D, seed=61, with_dout=True)
+    qd, kd, vd, dod = _to_dev(q, k, v, do)
+    order = chunk_order(n, seed=3)
+    out, lse, o_acc = ba.ring_forward(qd, kd, vd, n, order, scale=scale)
+    got = ba.ring_backward(qd, kd, vd, out, dod, lse, n, order, scale=scale)
+    torch.cuda.synchronize()
+    from oracle import attention_forward
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), scale=scale)
+    eo = float(np.abs(f64(o_acc) - o_ref).max())
+    el = float(np.abs(f64(lse) - l_ref).max())
+    log(f"scale={scale} fwd: max|O-ref| {eo:.3e} max|LSE-ref| {el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do), scale=scale)[:3]
+    _check_grads(f"scale={scale} bwd ring n={n}", got, ref)
