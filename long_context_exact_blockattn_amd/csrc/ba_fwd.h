@@ -38,7 +38,8 @@ struct FwdArgs {
   int32_t causal, accumulate, o_f32;
   int32_t s2_group, s2_shift_head0;
   float scale_log2;  // tau * log2(e)
-  int64_t n_qtiles;
+  int64_t n_qtiles;  // query tiles per (batch, head)
+  int64_t n_ranks;   // of which launched: the n_ranks longest (the rest have no allowed key)
   int64_t n_items;
 };
 
@@ -75,8 +76,8 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
 
   // ---- work item
   const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
-  const int64_t bh = pid / a.n_qtiles;
-  const int64_t w = pid % a.n_qtiles;
+  const int64_t bh = pid / a.n_ranks;
+  const int64_t w = pid % a.n_ranks;
   const int b = (int)(bh / a.Hq);
   const int h = (int)(bh % a.Hq);
   const int kvh = h / a.grp;

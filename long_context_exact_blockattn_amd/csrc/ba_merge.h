@@ -86,4 +86,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #endif
 }
 
+// Final bf16 store of rows a ring step does not reach: o_final = bf16(o_acc)
+// (round to nearest even) for rows [0, rows) of every (batch, head); the
+// running pair itself is left as it is.  HBM-bound like the merge: one thread
+// converts 8 consecutive elements, consecutive threads consecutive memory.
+struct StoreArgs {
+  const float* o_acc;
+  bf16* o_final;
+  int64_t s_b, s_s, s_h;
+  int64_t rows;
+  int32_t Hq, D;
+  int64_t n_threads;
+};
+
+__global__ __launch_bounds__(256) void store_final_kernel(StoreArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.n_threads) return;
+  const int cpr = a.D / 8;
+  const int64_t rowid = g / cpr;
+  const int c = (int)(g % cpr);
+  const int h = (int)(rowid % a.Hq);
+  const int64_t s = (rowid / a.Hq) % a.rows;
+  const int64_t b = rowid / ((int64_t)a.Hq * a.rows);
+  const int64_t off = b * a.s_b + s * a.s_s + h * a.s_h + 8 * c;
+  const f32x4 x0 = *(const f32x4*)(a.o_acc + off);
+  const f32x4 x1 = *(const f32x4*)(a.o_acc + off + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = (bf16)x0[e]; r[4 + e] = (bf16)x1[e]; }
+  *(bf16x8*)(a.o_final + off) = r;
+#endif
+}
+
 }  // namespace ba

@@ -99,8 +99,33 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.s2_shift_head0 = s2 ? s2->shift_head0 : 0;
   a.scale_log2 = scale_of(d) * kLog2e;
   a.n_qtiles = ceil_div(d->seqlen_q, kFwdBM);
-  a.n_items = (int64_t)d->batch * d->heads_q * a.n_qtiles;
+  // ACCUMULATE leaves rows the chunk cannot reach untouched, so causal query
+  // tiles wholly before the chunk are not launched (they are the last ranks of
+  // the longest-first order); their final bf16 store, if asked for, is a plain
+  // conversion of the running output
+  int64_t skip_qt = 0;
+  if (!s2 && d->causal && mode == BA_ACCUMULATE) {
+    int64_t first_row = d->seqlen_k > 0 ? d->k_pos0 - d->q_pos0 : d->seqlen_q;
+    first_row = first_row < 0 ? 0 : (first_row > d->seqlen_q ? d->seqlen_q : first_row);
+    skip_qt = first_row / kFwdBM;
+  }
+  a.n_ranks = a.n_qtiles - skip_qt;
+  a.n_items = (int64_t)d->batch * d->heads_q * a.n_ranks;
   if (a.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
+  if (o_final && skip_qt > 0) {
+    StoreArgs st;
+    st.o_acc = (const float*)o;
+    st.o_final = (bf16*)o_final;
+    st.s_b = d->q_stride[0]; st.s_s = d->q_stride[1]; st.s_h = d->q_stride[2];
+    st.rows = skip_qt * kFwdBM;
+    st.Hq = d->heads_q; st.D = d->head_dim;
+    st.n_threads = (int64_t)d->batch * st.rows * d->heads_q * (d->head_dim / 8);
+    const int64_t blocks = ceil_div(st.n_threads, 256);
+    if (blocks > 0x7fffffffLL) return BA_ERR_SHAPE;
+    hipLaunchKernelGGL(store_final_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, st);
+    if ((r = launched())) return r;
+  }
+  if (a.n_items == 0) return BA_OK;
   const dim3 grid((unsigned)a.n_items), block(kFwdThreads);
   if (d->head_dim == 128)
     hipLaunchKernelGGL(fwd_kernel<128>, grid, block, 0, stream, a);
