@@ -119,6 +119,34 @@ def test_accumulate_empty_chunk_is_identity():
     assert torch.equal(fin, o0.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("S,k0", [(300, 300), (300, 270), (1000, 130)])
+def test_accumulate_late_chunk_ragged(S, k0):
+    # ACCUMULATE with a chunk that starts at global position k0: the query tiles wholly before
+    # it are not launched and their final bf16 store comes from the conversion kernel; the
+    # tile holding k0 is computed (its earlier rows unchanged); rows at or after k0 merge
+    H, D = 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=17 + k0)
+    qd, kd, vd = _to_dev(q, k, v)
+    first = S // 2
+    o = torch.empty((1, S, H, D), device=dev())
+    lse = torch.empty((1, H, S), device=dev())
+    fin = torch.full((1, S, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
+    ba.blockattn_fwd(qd, kd[:, :first], vd[:, :first], o, lse)
+    o0, l0 = o.clone(), lse.clone()
+    n2 = min(S - first, 64)
+    ba.blockattn_fwd(qd, kd[:, first:first + n2], vd[:, first:first + n2], o, lse, mode=ba.BA_ACCUMULATE,
+                     k_pos0=k0, o_final=fin)
+    torch.cuda.synchronize()
+    # rows before k0 are untouched, and their bf16 output is the rounding of the running output
+    assert torch.equal(o[:, :k0], o0[:, :k0]) and torch.equal(lse[:, :, :k0], l0[:, :, :k0])
+    assert torch.equal(fin, o.to(torch.bfloat16))
+    # the merged pair equals attention over both key sets at their positions
+    o_a, l_a = attention_forward(f64(q), f64(k[:, :first]), f64(v[:, :first]))
+    o_b, l_b = attention_forward(f64(q), f64(k[:, first:first + n2]), f64(v[:, first:first + n2]), k_pos0=k0)
+    o_ref, l_ref = lse_merge(o_a, l_a, o_b, l_b)
+    _check_pair(f"late chunk S={S} k0={k0}", o, lse, o_ref, l_ref, fin)
+
+
 def test_peaked_softmax():
     S, H, D = 1024, 2, 128
     q, k, v = make_inputs(1, S, H, H, D, seed=21, q_scale=4.0)
