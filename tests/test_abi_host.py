@@ -243,3 +243,20 @@ def test_ring_drivers_reject_bad_chunk_orders():
             ring_forward(q, q, q, 4, bad)
         with pytest.raises(ValueError, match="permutation"):
             ring_backward(q, q, q, q, q, lse, 4, bad)
+
+
+@pytest.mark.parametrize("Sq,Sk,q0,k0", [(1000, 250, 0, 750), (1000, 250, 0, 130), (512, 64, 0, 512),
+                                         (300, 100, 50, 280), (2048, 512, 0, 1536), (256, 100, 300, 0)])
+def test_unreached_causal_tiles_are_the_last_ranks(lib, Sq, Sk, q0, k0):
+    # an ACCUMULATE ring step launches only the first (n_qtiles - skip) ranks, skip = the query
+    # tiles wholly before the chunk; this needs those tiles to have no key tile to visit and
+    # to come last in the visiting order
+    d = _desc(Sq=Sq, Sk=Sk, q0=q0, k0=k0)
+    bm, _ = _lib.debug_tile_sizes(d.head_dim)
+    skip = min(max(k0 - q0, 0), Sq) // bm
+    rec = _lib.debug_fwd_schedule(d, head=0)
+    visited = [int(r) for r in dict.fromkeys(rec[:, 0])]  # query tiles' first rows, visiting order
+    assert all(r >= skip * bm for r in visited), "a skipped tile has work"
+    n_qtiles = -(-Sq // bm)
+    launched = sorted(range(skip, n_qtiles), reverse=True)  # ranks 0 .. n_qtiles - skip - 1
+    assert [r // bm for r in visited] == launched[:len(visited)]
