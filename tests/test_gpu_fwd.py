@@ -119,18 +119,18 @@ def test_accumulate_empty_chunk_is_identity():
     assert torch.equal(fin, o0.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("S,k0", [(300, 300), (300, 270), (1000, 130)])
-def test_accumulate_late_chunk_ragged(S, k0):
+@pytest.mark.parametrize("B,S,k0", [(1, 300, 300), (1, 300, 270), (1, 1000, 130), (2, 700, 390)])
+def test_accumulate_late_chunk_ragged(B, S, k0):
     # ACCUMULATE with a chunk that starts at global position k0: the query tiles wholly before
     # it are not launched and their final bf16 store comes from the conversion kernel; the
     # tile holding k0 is computed (its earlier rows unchanged); rows at or after k0 merge
     H, D = 2, 128
-    q, k, v = make_inputs(1, S, H, H, D, seed=17 + k0)
+    q, k, v = make_inputs(B, S, H, H, D, seed=17 + k0)
     qd, kd, vd = _to_dev(q, k, v)
     first = S // 2
-    o = torch.empty((1, S, H, D), device=dev())
-    lse = torch.empty((1, H, S), device=dev())
-    fin = torch.full((1, S, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
+    o = torch.empty((B, S, H, D), device=dev())
+    lse = torch.empty((B, H, S), device=dev())
+    fin = torch.full((B, S, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
     ba.blockattn_fwd(qd, kd[:, :first], vd[:, :first], o, lse)
     o0, l0 = o.clone(), lse.clone()
     n2 = min(S - first, 64)
@@ -144,7 +144,7 @@ def test_accumulate_late_chunk_ragged(S, k0):
     o_a, l_a = attention_forward(f64(q), f64(k[:, :first]), f64(v[:, :first]))
     o_b, l_b = attention_forward(f64(q), f64(k[:, first:first + n2]), f64(v[:, first:first + n2]), k_pos0=k0)
     o_ref, l_ref = lse_merge(o_a, l_a, o_b, l_b)
-    _check_pair(f"late chunk S={S} k0={k0}", o, lse, o_ref, l_ref, fin)
+    _check_pair(f"late chunk B={B} S={S} k0={k0}", o, lse, o_ref, l_ref, fin)
 
 
 def test_peaked_softmax():
