@@ -180,7 +180,8 @@ def test_lse_merge_standalone(part_dtype):
     lb = torch.randn(B, H, S, generator=g) * 3
     la[0, 0, :10] = float("-inf")
     lb[0, 0, 5:15] = float("-inf")
-    oa[0, :10, 0] = float("nan")      # O of an empty pair is never read
+    oa[0, :10, 0] = float("nan")      # the O of an empty pair does not reach the result
+    ob[0, 5:15, 0] = float("nan")
     o_ref, l_ref = lse_merge(f64(oa), f64(la), f64(ob), f64(lb))
     oad, lad, obd, lbd = _to_dev(oa, la, ob, lb)
     fin = torch.empty((B, S, H, D), device=dev(), dtype=torch.bfloat16)
