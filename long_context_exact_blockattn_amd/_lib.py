@@ -149,13 +149,18 @@ def _bshd_strides(t, name):
     return (t.stride(0), t.stride(1), t.stride(2))
 
 
-def _same_layout(ref, t, name, shape=None):
+def _same_layout(ref, t, name, shape=None, ref_name="q"):
+    """t has ref's shape and, on every axis longer than one, ref's stride: the kernels address
+    every query-shaped tensor with q's strides, and an axis of length one is never stepped along
+    (torch keeps arbitrary strides there, e.g. after .contiguous() of a slice of a batch of one)."""
     if t is None:
         return
     if tuple(t.shape) != tuple(ref.shape if shape is None else shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
-    if t.dim() == 4 and _bshd_strides(t, name) != _bshd_strides(ref, "q"):
-        raise ValueError(f"{name} must have the same (b, s, h) strides as q")
+    if t.dim() == 4:
+        ts, rs = _bshd_strides(t, name), _bshd_strides(ref, ref_name)
+        if any(n > 1 and a != b for n, a, b in zip(t.shape[:3], ts, rs)):
+            raise ValueError(f"{name} must have the same (b, s, h) strides as {ref_name}")
 
 
 def _stats_ok(t, shape, name):
@@ -196,8 +201,7 @@ def blockattn_fwd(q, k, v, o, lse, *, mode=BA_OVERWRITE, o_final=None, q_pos0=0,
     _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
                  (lse, "lse", "float32"), (o_final, "o_final", "bfloat16")])
     desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
-    if tuple(v.shape) != tuple(k.shape) or _bshd_strides(v, "v") != _bshd_strides(k, "k"):
-        raise ValueError("v must match k in shape and strides")
+    _same_layout(k, v, "v", ref_name="k")
     _same_layout(q, o, "o")
     _same_layout(q, o_final, "o_final")
     _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
@@ -225,8 +229,7 @@ def s2attn_fwd(q, k, v, o, lse, *, group, shift_head0, scale=None, stream=None):
     _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
                  (lse, "lse", "float32")])
     desc = make_desc(q, k, causal=True, scale=scale)
-    if tuple(v.shape) != tuple(k.shape) or _bshd_strides(v, "v") != _bshd_strides(k, "k"):
-        raise ValueError("v must match k in shape and strides")
+    _same_layout(k, v, "v", ref_name="k")
     _same_layout(q, o, "o")
     _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
     s2 = BaS2Desc(int(group), int(shift_head0))
@@ -243,8 +246,7 @@ def _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final):
     for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
         _same_layout(q, t, n)
     for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
-        if tuple(t.shape) != tuple(k.shape) or _bshd_strides(t, n) != _bshd_strides(k, "k"):
-            raise ValueError(f"{n} must match k in shape and strides")
+        _same_layout(k, t, n, ref_name="k")
     if dk.dtype != dv.dtype:
         raise ValueError("dk and dv must share a dtype")
     shape = (q.shape[0], q.shape[2], q.shape[1])

@@ -260,3 +260,24 @@ def test_unreached_causal_tiles_are_the_last_ranks(lib, Sq, Sk, q0, k0):
     n_qtiles = -(-Sq // bm)
     launched = sorted(range(skip, n_qtiles), reverse=True)  # ranks 0 .. n_qtiles - skip - 1
     assert [r // bm for r in visited] == launched[:len(visited)]
+
+
+def test_binding_layout_check_ignores_length_one_axes():
+    """The kernels address every query-shaped tensor with q's strides; an axis of length one is
+    never stepped along, so its stride may differ (torch keeps a slice's batch stride in
+    .contiguous() of a batch of one), while a real stride mismatch is refused."""
+    import torch
+    q = torch.zeros(1, 1000, 4, 128)[:, 300:700].contiguous()
+    o = torch.zeros(1, 400, 4, 128)
+    assert q.stride(0) != o.stride(0)
+    _lib._same_layout(q, o, "o")
+    q2 = torch.zeros(2, 1000, 4, 128)[:, 300:700]
+    with pytest.raises(ValueError, match="strides as q"):
+        _lib._same_layout(q2, torch.zeros(2, 400, 4, 128), "o")
+    k = torch.zeros(2, 64, 1, 128)
+    v = torch.zeros(2, 64, 3, 128)[:, :, 1:2]  # sequence stride 384 against k's 128
+    with pytest.raises(ValueError, match="strides as k"):
+        _lib._same_layout(k, v, "v", ref_name="k")
+    # one head: only the (unused) head stride differs
+    v1 = torch.zeros(2 * 64 * 128 + 1000).as_strided((2, 64, 1, 128), (8192, 128, 999, 1))
+    _lib._same_layout(k, v1, "v", ref_name="k")

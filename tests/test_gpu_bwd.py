@@ -237,3 +237,48 @@ def test_explicit_softmax_scale_forward_and_backward(scale):
     assert eo <= 1e-2 and el <= 1e-3
     ref = attention_backward(f64(q), f64(k), f64(v), f64(do), scale=scale)[:3]
     _check_grads(f"scale={scale} bwd ring n={n}", got, ref)
+
+
+def test_query_block_at_an_offset_forward_and_backward():
+    """One device's view of a ring: its query block holds rows [300, 700) of a 1000-token sequence
+    (q_pos0 = 300) and meets the four key/value chunks in a shuffled order, the last of which lies
+    wholly after the block.  dQ of the block is the block's rows of the full dQ; the chunk
+    gradients are the block's contribution, i.e. the full dK, dV with dO zero outside the block;
+    the chunk after the block gets exact zeros."""
+    B, S, Hq, Hkv, D = 1, 1000, 4, 2, 128
+    a0, a1 = 300, 700
+    q, k, v, do = make_inputs(B, S, Hq, Hkv, D, seed=23, with_dout=True)
+    dom = do.clone()
+    dom[:, :a0] = 0
+    dom[:, a1:] = 0
+    dq_r, dk_r, dv_r, o_r, l_r = attention_backward(f64(q), f64(k), f64(v), f64(dom))
+    qd, kd, vd = _to_dev(q[:, a0:a1].contiguous(), k, v)
+    dod = do[:, a0:a1].contiguous().to(dev())
+    bounds = [(0, 250), (250, 500), (500, 750), (750, 1000)]
+    order = [2, 0, 3, 1]
+    n = a1 - a0
+    o_acc = torch.empty(B, n, Hq, D, device=dev())
+    lse = torch.empty(B, Hq, n, device=dev())
+    o = torch.empty(B, n, Hq, D, device=dev(), dtype=torch.bfloat16)
+    for t, c in enumerate(order):
+        c0, c1 = bounds[c]
+        ba.blockattn_fwd(qd, kd[:, c0:c1], vd[:, c0:c1], o_acc, lse,
+                         mode=ba.BA_OVERWRITE if t == 0 else ba.BA_ACCUMULATE,
+                         o_final=o if t == len(order) - 1 else None, q_pos0=a0, k_pos0=c0)
+    delta = torch.empty(B, Hq, n, device=dev())
+    dq_acc = torch.zeros(B, n, Hq, D, device=dev())
+    dq = torch.empty(B, n, Hq, D, device=dev(), dtype=torch.bfloat16)
+    dk = torch.full(k.shape, float("nan"), device=dev(), dtype=torch.bfloat16)
+    dv = torch.full(v.shape, float("nan"), device=dev(), dtype=torch.bfloat16)
+    for t, c in enumerate(order):
+        c0, c1 = bounds[c]
+        flags = (_lib.BA_BWD_COMPUTE_DELTA if t == 0 else 0) | (_lib.BA_BWD_FINALIZE_DQ if t == len(order) - 1 else 0)
+        ba.blockattn_bwd(qd, kd[:, c0:c1], vd[:, c0:c1], o, dod, lse, delta, dq_acc, dk[:, c0:c1],
+                         dv[:, c0:c1], dq_final=dq, flags=flags, q_pos0=a0, k_pos0=c0)
+    torch.cuda.synchronize()
+    eo = float(np.abs(f64(o_acc) - o_r[:, a0:a1]).max())
+    el = float(np.abs(f64(lse) - l_r[:, :, a0:a1]).max())
+    log(f"query block at offset {a0}: max|O-ref| {eo:.3e} max|LSE-ref| {el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3
+    _check_grads("query block at an offset", (dq, dk, dv), (dq_r[:, a0:a1], dk_r, dv_r))
+    assert not dk[:, 750:].float().abs().max().item() and not dv[:, 750:].float().abs().max().item()
