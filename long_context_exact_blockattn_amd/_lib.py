@@ -179,9 +179,15 @@ def make_desc(q, k, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
     desc.q_pos0, desc.k_pos0 = int(q_pos0), int(k_pos0)
     desc.causal = 1 if causal else 0
     desc.scale = 0.0 if scale is None else float(scale)
-    desc.q_stride[:] = _bshd_strides(q, "q")
-    desc.kv_stride[:] = _bshd_strides(k, "k") if k is not None else (0, 0, 0)
+    desc.q_stride[:] = _used_strides(q, "q")
+    desc.kv_stride[:] = _used_strides(k, "k") if k is not None else (0, 0, 0)
     return desc
+
+
+def _used_strides(t, name):
+    """(b, s, h) strides with 0 on axes of length one: the kernels never step along those, and
+    torch may leave any value there (which the library would check against its stride rules)."""
+    return tuple(0 if n == 1 else st for n, st in zip(t.shape[:3], _bshd_strides(t, name)))
 
 
 def _dtype_code(t, name):

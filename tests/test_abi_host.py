@@ -281,3 +281,16 @@ def test_binding_layout_check_ignores_length_one_axes():
     # one head: only the (unused) head stride differs
     v1 = torch.zeros(2 * 64 * 128 + 1000).as_strided((2, 64, 1, 128), (8192, 128, 999, 1))
     _lib._same_layout(k, v1, "v", ref_name="k")
+
+
+def test_descriptor_zeroes_strides_of_length_one_axes(lib):
+    """A batch of one sliced at an odd element offset has an odd batch stride that no kernel ever
+    uses; the descriptor carries 0 there, so the call passes the library's stride rules."""
+    import torch
+    x = torch.zeros(1, 300, 2, 128).as_strided((1, 300, 2, 128), (12345, 256, 128, 1))
+    d = _lib.make_desc(x, x)
+    assert tuple(d.q_stride) == (0, 256, 128) and tuple(d.kv_stride) == (0, 256, 128)
+    # validation passes the strides and stops at the (fake) misaligned pointer instead
+    assert _fwd(lib, d, q=FAKE + 2) == _lib.BA_ERR_ALIGN
+    y = torch.zeros(2, 1, 2, 128)
+    assert tuple(_lib.make_desc(y, y).q_stride) == (256, 0, 128)
