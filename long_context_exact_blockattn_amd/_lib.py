@@ -171,7 +171,12 @@ def _stats_ok(t, shape, name):
 
 
 def make_desc(q, k, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
+    if q.dim() != 4 or (k is not None and k.dim() != 4):
+        raise ValueError("q and k must be [B, S, H, D]")
     b, sq, hq, d = q.shape
+    # the descriptor carries one batch size and one head size for every tensor of the call
+    if k is not None and (k.shape[0] != b or k.shape[3] != d):
+        raise ValueError(f"k {tuple(k.shape)} must have q's batch ({b}) and head_dim ({d})")
     sk, hkv = (k.shape[1], k.shape[2]) if k is not None else (0, hq)
     desc = BaDesc()
     desc.batch, desc.heads_q, desc.heads_kv, desc.head_dim = b, hq, hkv, d

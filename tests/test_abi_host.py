@@ -294,3 +294,18 @@ def test_descriptor_zeroes_strides_of_length_one_axes(lib):
     assert _fwd(lib, d, q=FAKE + 2) == _lib.BA_ERR_ALIGN
     y = torch.zeros(2, 1, 2, 128)
     assert tuple(_lib.make_desc(y, y).q_stride) == (256, 0, 128)
+
+
+def test_descriptor_refuses_k_of_another_batch_or_head_size():
+    """The descriptor holds one batch size and one head size: a k that differs in either would be
+    read past its end (or, with a batch of one, silently reused), so the binding refuses it."""
+    import torch
+    q = torch.zeros(2, 64, 4, 128)
+    with pytest.raises(ValueError, match="batch"):
+        _lib.make_desc(q, torch.zeros(1, 64, 2, 128))
+    with pytest.raises(ValueError, match="head_dim"):
+        _lib.make_desc(q, torch.zeros(2, 64, 2, 64))
+    with pytest.raises(ValueError, match=r"\[B, S, H, D\]"):
+        _lib.make_desc(q, torch.zeros(2, 64, 128))
+    d = _lib.make_desc(q, torch.zeros(2, 32, 2, 128))  # other length and head count: the ABI's business
+    assert (d.batch, d.heads_q, d.heads_kv, d.seqlen_q, d.seqlen_k) == (2, 4, 2, 64, 32)
