@@ -83,7 +83,8 @@ typedef struct {
   int64_t q_pos0;     /* global position of query row 0 */
   int64_t k_pos0;     /* global position of key row 0 (the ring step's chunk offset) */
   int32_t causal;     /* 1: causal mask on global positions; 0: every key allowed */
-  float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim); the forward and backward
+                         return BA_ERR_SHAPE for NaN or inf */
   int64_t q_stride[3];  /* (b, s, h) element strides of every query-shaped tensor */
   int64_t kv_stride[3]; /* (b, s, h) element strides of every key-shaped tensor */
 } ba_desc;

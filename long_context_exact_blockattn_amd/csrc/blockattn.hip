@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "ba_bwd.h"
 #include "ba_common.h"
@@ -74,6 +75,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
              void* o, int32_t o_dtype, float* lse, int32_t mode, void* o_final, hipStream_t stream) {
   int r = check_desc(d);
   if (r) return r;
+  if (!std::isfinite(d->scale)) return BA_ERR_SHAPE;
   if (s2 && (r = check_s2(d, s2))) return r;
   if (mode != BA_OVERWRITE && mode != BA_ACCUMULATE) return BA_ERR_MODE;
   if (o_dtype != BA_F32 && o_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;
@@ -139,6 +141,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
              void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags, hipStream_t stream) {
   int r = check_desc(d);
   if (r) return r;
+  if (!std::isfinite(d->scale)) return BA_ERR_SHAPE;
   if (s2 && (r = check_s2(d, s2))) return r;
   if (flags & ~(BA_BWD_COMPUTE_DELTA | BA_BWD_FINALIZE_DQ)) return BA_ERR_MODE;
   if (dkv_dtype != BA_F32 && dkv_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;

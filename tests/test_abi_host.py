@@ -70,6 +70,15 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, _desc(), odt=_lib.BA_BF16, mode=_lib.BA_ACCUMULATE) == _lib.BA_ERR_MODE
     assert _fwd(lib, _desc(), odt=7) == _lib.BA_ERR_UNSUPPORTED
     assert _fwd(lib, _desc(causal=2)) == _lib.BA_ERR_SHAPE
+    for bad_scale in (float("nan"), float("inf"), float("-inf")):
+        d = _desc()
+        d.scale = bad_scale
+        assert _fwd(lib, d) == _lib.BA_ERR_SHAPE
+        P = ctypes.c_void_p
+        F = P(FAKE)
+        assert lib.blockattn_bwd(ctypes.byref(d), F, F, F, F, F, F, F, F, F, F, 1, None, 0, None) == _lib.BA_ERR_SHAPE
+        # the merge does not use the scale
+        assert lib.lse_merge(ctypes.byref(d), F, F, P(FAKE + 4), 0, F, None, None) == _lib.BA_ERR_ALIGN
 
 
 def test_zero_size_returns_ok_without_launch(lib):
