@@ -396,8 +396,9 @@ def _counters(kernel_key, src_path, workload):
                                 "lds_per_mfma", "wave_waiting")}
 
 
-def counter_summary(d, out=None):
-    """MFMA-busy beside VALU-busy for the forward kernel, from one rocprofv3 --pmc pass with COUNTERS.
+def counter_summary(d, out=None, kernel=None):
+    """MFMA-busy beside VALU-busy for one kernel (default: the D=128 forward), from one rocprofv3
+    --pmc pass with COUNTERS; the summary record is written for the forward only.
 
     Per dispatch: cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs); MFMA busy =
     SQ_VALU_MFMA_BUSY_CYCLES (32 per MFMA, summed over SIMDs) / (1024 SIMDs x cycles); VALU busy is
@@ -410,7 +411,7 @@ def counter_summary(d, out=None):
         con = sqlite3.connect(db)
         q = "select dispatch_id, kernel_name, counter_name, value from counters_collection"
         for disp, name, cname, val in con.execute(q):
-            if "fwd_kernel<128>" in name:
+            if (kernel or "fwd_kernel<128>") in name:
                 rec = per.setdefault((db, disp), {})
                 rec[cname] = rec.get(cname, 0.0) + val
     rows = []
@@ -430,10 +431,10 @@ def counter_summary(d, out=None):
     tot = sum(r["mfma"] for r in rows)
     keys = ("mfma_busy", "valu_busy_est", "valu_per_mfma", "trans_per_mfma", "lds_per_mfma", "wave_waiting")
     avg = {k: sum(r[k] * r["mfma"] for r in rows) / tot for k in keys}
-    print(f"{len(rows)} dispatches of fwd_kernel<128>; MFMA-weighted averages:")
+    print(f"{len(rows)} dispatches of {kernel or 'fwd_kernel<128>'}; MFMA-weighted averages:")
     for k in keys:
         print(f"  {k:15s} {avg[k]:8.3f}")
-    if out:
+    if out and kernel is None:
         rec = {"kernel": "ba::fwd_kernel<128>", "workload": "llama2_7b_s32k_ring8",
                "kernel_source_sha": _src_sha(FWD_SRC), "dispatches": len(rows),
                "command": f"rocprofv3 --pmc {COUNTERS} -d {d} -o busy -- python -u bench.py --steps 1 "
@@ -593,13 +594,16 @@ def main():
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="print MFMA-busy and VALU-busy of the forward kernel from a rocprofv3 --pmc run "
                          "with the counters in bench.COUNTERS")
+    ap.add_argument("--counter-kernel", metavar="NAME",
+                    help="with --counter-summary: summarise this kernel instead of the forward (printed only)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel statistics of a rocprofv3 --kernel-trace output directory")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.counter_summary:
-        counter_summary(args.counter_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_counters.json"))
+        counter_summary(args.counter_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_counters.json"),
+                        kernel=args.counter_kernel)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
