@@ -109,3 +109,20 @@ def test_counter_record_is_reported_only_when_current(tmp_path, monkeypatch):
     rec["kernel_source_sha"] = "f" * 16
     json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_counters.json"), "w"))
     assert bench._counters("fwd_kernel_d128", bench.FWD_SRC, "llama2_7b_s32k_ring8") is None
+
+
+def test_counter_summary_of_another_kernel_prints_only(tmp_path, capsys):
+    rows = []
+    for disp, name in ((1, "void ba::bwd_dkdv_kernel<128>(ba::BwdArgs)"), (2, "void ba::fwd_kernel<128>(ba::FwdArgs)")):
+        for cname, val in (("GRBM_GUI_ACTIVE", 8000.0), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 500.0),
+                           ("SQ_INSTS_MFMA", 100.0), ("SQ_INSTS_VALU", 600.0), ("SQ_INSTS_VALU_TRANS_F32", 50.0),
+                           ("SQ_INSTS_LDS", 190.0), ("SQ_WAIT_ANY", 40.0), ("SQ_WAVE_CYCLES", 100.0)):
+            rows.append((disp, name, cname, val))
+    _counters_db(str(tmp_path / "p" / "a_results.db"), rows)
+    out = str(tmp_path / "rec.json")
+    bench.counter_summary(str(tmp_path / "p"), out, kernel="bwd_dkdv_kernel<128>")
+    text = capsys.readouterr().out
+    assert "1 dispatches of bwd_dkdv_kernel<128>" in text
+    # 500 busy cycles per SIMD over 1000 cycles; 1.9 LDS instructions per MFMA
+    assert "mfma_busy          0.500" in text and "lds_per_mfma       1.900" in text
+    assert not os.path.exists(out)  # the summary record is the forward's only
