@@ -601,6 +601,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.counter_summary:
         counter_summary(args.counter_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_counters.json"),
                         kernel=args.counter_kernel)

@@ -126,3 +126,9 @@ def test_counter_summary_of_another_kernel_prints_only(tmp_path, capsys):
     # 500 busy cycles per SIMD over 1000 cycles; 1.9 LDS instructions per MFMA
     assert "mfma_busy          0.500" in text and "lds_per_mfma       1.900" in text
     assert not os.path.exists(out)  # the summary record is the forward's only
+
+
+def test_step_counts_are_checked():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--steps" in r.stderr and r.stdout == ""
