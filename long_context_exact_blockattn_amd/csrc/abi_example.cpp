@@ -9,7 +9,10 @@
 //     tolerances (the two round P to bf16 against different running maxima and
 //     merge in fp32), and the bf16 output is the rounding of the fp32 one -- the
 //     order independence of the blockwise method (Ring Attention summary,
-//     Summary).
+//     Summary);
+//  3. the backward over the same ring (delta on the first step, dQ accumulated
+//     in fp32 and converted on the last, dK and dV written per chunk) equals one
+//     backward call over all keys within a relative L2 of 1e-2 per gradient.
 // Prints one line "abi_example ok ..." and exits 0, or prints the failure and
 // exits 1.
 #include <hip/hip_runtime_api.h>
@@ -166,10 +169,68 @@ int main() {
     fprintf(stderr, "ring vs one call: max|dO| %.3e max|dLSE| %.3e\n", max_o, max_l);
     return fail("ring result differs from the one-call result");
   }
+
+  // ---- 3. backward: the ring of chunks against one call over all keys
+  std::vector<uint16_t> hdo(n);
+  for (int64_t i = 0; i < n; ++i) hdo[i] = to_bf16(g.next());
+  void *dout, *dq1, *dk1, *dv1, *dq2, *dk2, *dv2;
+  float *delta, *dqa1, *dqa2;
+  HIP_OK(hipMalloc(&dout, n * 2));
+  HIP_OK(hipMalloc(&dq1, n * 2));
+  HIP_OK(hipMalloc(&dk1, n * 2));
+  HIP_OK(hipMalloc(&dv1, n * 2));
+  HIP_OK(hipMalloc(&dq2, n * 2));
+  HIP_OK(hipMalloc(&dk2, n * 2));
+  HIP_OK(hipMalloc(&dv2, n * 2));
+  HIP_OK(hipMalloc((void**)&delta, n_rows * 4));
+  HIP_OK(hipMalloc((void**)&dqa1, n * 4));
+  HIP_OK(hipMalloc((void**)&dqa2, n * 4));
+  HIP_OK(hipMemcpy(dout, hdo.data(), n * 2, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(dqa1, 0, n * 4));
+  HIP_OK(hipMemset(dqa2, 0, n * 4));
+  if (blockattn_bwd(&d, q, k, v, o_bf16, dout, lse_ring, delta, dqa1, dk1, dv1, BA_BF16, dq1,
+                    BA_BWD_COMPUTE_DELTA | BA_BWD_FINALIZE_DQ, st) != BA_OK)
+    return fail("one-shot backward");
+  for (int t = 0; t < n_chunks; ++t) {
+    ba_desc dc = d;
+    dc.seqlen_k = C;
+    dc.k_pos0 = order[t] * C;
+    const int64_t koff = dc.k_pos0 * strides[1] * 2;
+    const int flags = (t == 0 ? BA_BWD_COMPUTE_DELTA : 0) | (t == n_chunks - 1 ? BA_BWD_FINALIZE_DQ : 0);
+    const int st_ = blockattn_bwd(&dc, q, (const char*)k + koff, (const char*)v + koff, o_bf16, dout, lse_ring,
+                                  delta, dqa2, (char*)dk2 + koff, (char*)dv2 + koff, BA_BF16, dq2, flags, st);
+    if (st_ != BA_OK) {
+      fprintf(stderr, "backward ring step %d: %s\n", t, blockattn_status_string(st_));
+      return 1;
+    }
+  }
+  HIP_OK(hipStreamSynchronize(st));
+  double rel[3];
+  void* const pairs[3][2] = {{dq1, dq2}, {dk1, dk2}, {dv1, dv2}};
+  std::vector<uint16_t> ga(n), gb(n);
+  for (int j = 0; j < 3; ++j) {
+    HIP_OK(hipMemcpy(ga.data(), pairs[j][0], n * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gb.data(), pairs[j][1], n * 2, hipMemcpyDeviceToHost));
+    double num = 0, den = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      const double x = from_bf16(ga[i]), y = from_bf16(gb[i]);
+      if (!isfinite(x) || !isfinite(y)) return fail("non-finite gradient");
+      num += (x - y) * (x - y);
+      den += x * x;
+    }
+    rel[j] = sqrt(num / (den > 0 ? den : 1.0));
+  }
+  if (rel[0] > 1e-2 || rel[1] > 1e-2 || rel[2] > 1e-2) {
+    fprintf(stderr, "backward ring vs one call: rel L2 dq %.3e dk %.3e dv %.3e\n", rel[0], rel[1], rel[2]);
+    return fail("ring backward differs from the one-call backward");
+  }
   printf("abi_example ok: ring of %d chunks vs one call over S=%lld keys: max|dO| %.3e, max|dLSE| %.3e; "
-         "first output %.6f\n", (int)n_chunks, (long long)S, max_o, max_l, from_bf16(ob[0]));
+         "backward rel L2 dq %.3e dk %.3e dv %.3e; first output %.6f\n", (int)n_chunks, (long long)S, max_o,
+         max_l, rel[0], rel[1], rel[2], from_bf16(ob[0]));
   hipFree(q); hipFree(k); hipFree(v); hipFree(o_ring); hipFree(o_one); hipFree(o_bf16);
   hipFree(lse_ring); hipFree(lse_one);
+  hipFree(dout); hipFree(dq1); hipFree(dk1); hipFree(dv1); hipFree(dq2); hipFree(dk2); hipFree(dv2);
+  hipFree(delta); hipFree(dqa1); hipFree(dqa2);
   hipStreamDestroy(st);
   return 0;
 }
