@@ -47,7 +47,7 @@ def test_ring_small_d64_seeded_order():
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S,Hq,Hkv,causal", [(1000, 2, 2, True), (333, 8, 2, True), (777, 4, 4, False),
-                                             (128, 2, 1, True), (1, 2, 2, True)])
+                                             (128, 2, 1, True), (1, 2, 2, True), (300, 1, 1, True)])
 def test_one_shot(D, S, Hq, Hkv, causal):
     q, k, v = make_inputs(1, S, Hq, Hkv, D, seed=S + D)
     qd, kd, vd = _to_dev(q, k, v)
