@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import (NEG_INF, S2Spec, allowed_mask, attention_backward, attention_forward,
-                    default_scale, lse_merge, ring_attention_forward, rows_forward)
+                    backward_delta, default_scale, lse_merge, ring_attention_forward, rows_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -69,6 +69,17 @@ def test_golden_backward_handworked():
     np.testing.assert_allclose(dq.ravel(), g["dq"], atol=1e-13)
     np.testing.assert_allclose(dk.ravel(), [_expr(e) for e in g["dk_exprs"]], atol=1e-13)
     np.testing.assert_allclose(dv.ravel(), g["dv"], atol=1e-13)
+
+
+def test_golden_backward_delta_handworked():
+    # Delta of the hand-worked example, from the hand-derived O and from the oracle's own O
+    g = _load("handworked_backward.json")
+    sh = (1, 2, 1, 1)
+    o, do = (np.array(g[n]).reshape(sh) for n in ("o", "dout"))
+    np.testing.assert_allclose(backward_delta(o, do).ravel(), g["delta"], atol=1e-13)
+    q, k, v = (np.array(g[n]).reshape(sh) for n in ("q", "k", "v"))
+    o_or, _ = attention_forward(q, k, v, scale=g["scale"], causal=True)
+    np.testing.assert_allclose(backward_delta(o_or, do).ravel(), g["delta"], atol=1e-13)
 
 
 def test_golden_s2_allowed_sets():
@@ -135,6 +146,53 @@ def test_bruteforce_forward(case):
     np.testing.assert_allclose(o, ob, atol=1e-12)
     assert np.array_equal(np.isinf(l), np.isinf(lb))
     np.testing.assert_allclose(l[np.isfinite(l)], lb[np.isfinite(lb)], atol=1e-12)
+
+
+def _brute_delta_by_probs(q, k, v, do, scale, allowed):
+    """Delta[b, h, i] as sum_j P_ij dP_ij, every quantity by plain loops: P from the scores,
+    dP_ij = dO_i . V_j.  Since sum_j P_ij V_j = O_i this equals dO_i . O_i, but it is built
+    without forming O, so a Delta taken from the wrong row, head or batch does not match."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    grp = Hq // Hkv
+    delta = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // grp
+            for i in range(Sq):
+                js = [j for j in range(Sk) if allowed(b, h, i, j)]
+                if not js:
+                    continue
+                s = {j: scale * sum(q[b, i, h, d] * k[b, j, kh, d] for d in range(D)) for j in js}
+                mx = max(s.values())
+                z = sum(math.exp(x - mx) for x in s.values())
+                for j in js:
+                    p = math.exp(s[j] - mx) / z
+                    dp = sum(do[b, i, h, d] * v[b, j, kh, d] for d in range(D))
+                    delta[b, h, i] += p * dp
+    return delta
+
+
+def _check_backward_delta(fn):
+    """Pin of backward_delta (or a stand-in fn with its signature): on B=2, S=6, Hq=4, Hkv=2,
+    D=3 (every axis a different length, so a wrong axis order cannot pass) it must equal the
+    pure-loop sum_j P_ij dP_ij, with the O it is given being the pure-loop forward's O."""
+    B, S, Hq, Hkv, D = 2, 6, 4, 2, 3
+    q = _rand((B, S, Hq, D), 160)
+    k = _rand((B, S, Hkv, D), 161)
+    v = _rand((B, S, Hkv, D), 162)
+    do = _rand((B, S, Hq, D), 163)
+    tau = 1.0 / math.sqrt(D)
+    allowed = lambda b, h, i, j: j <= i
+    o_bf, _ = _brute_forward(q, k, v, tau, allowed)
+    want = _brute_delta_by_probs(q, k, v, do, tau, allowed)
+    got = fn(o_bf, do)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+def test_bruteforce_backward_delta():
+    _check_backward_delta(backward_delta)
 
 
 def test_bruteforce_forward_s2():
@@ -415,6 +473,27 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     p, _ = oa._softmax_rows(s, allowed_mask(np.arange(S), np.arange(S)))
     ds_wrong = p * (dd[0, :, 0] @ vv[0, :, 0].T)
     assert np.abs((tau * ds_wrong.T @ qq[0, :, 0]).sum(axis=0)).max() > 1e-3
+
+
+@pytest.mark.parametrize("mistake", ["reshape_not_transpose", "head_shifted", "row_shifted",
+                                     "batch_swapped", "summed_over_rows"])
+def test_delta_pin_catches_planted_mistakes(mistake):
+    # plausible mistakes in Delta = rowsum(dO * O), each planted in a stand-in for the oracle's
+    # backward_delta; the brute-force pin must reject every one
+    def bad(o, do):
+        prod = o * do
+        if mistake == "reshape_not_transpose":     # [B, S, H] reinterpreted as [B, H, S]
+            return np.sum(prod, axis=-1).reshape(o.shape[0], o.shape[2], o.shape[1])
+        if mistake == "head_shifted":              # dO of the neighbouring head
+            return np.transpose(np.sum(o * np.roll(do, 1, axis=2), axis=-1), (0, 2, 1))
+        if mistake == "row_shifted":               # dO of the previous row
+            return np.transpose(np.sum(o * np.roll(do, 1, axis=1), axis=-1), (0, 2, 1))
+        if mistake == "batch_swapped":
+            return np.transpose(np.sum(o * do[::-1], axis=-1), (0, 2, 1))
+        return np.transpose(np.broadcast_to(np.sum(prod, axis=(1, 3))[:, None, :],
+                                            prod.shape[:3]), (0, 2, 1))
+    with pytest.raises(AssertionError):
+        _check_backward_delta(bad)
 
 
 # ---------------------------------------------------------------- sampled backward helpers
