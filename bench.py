@@ -29,6 +29,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "causal attention fwd/bwd TFLOP/s and % bf16 MFMA peak at S=32K-128K, D=128"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 FWD_SRC = os.path.join(ROOT, "long_context_exact_blockattn_amd", "csrc", "ba_fwd.h")
+BWD_SRC = os.path.join(ROOT, "long_context_exact_blockattn_amd", "csrc", "ba_bwd.h")
 
 
 def _src_sha(path):
@@ -36,9 +37,9 @@ def _src_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel_key, src_path, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this
-    workload and the kernel source has not changed since."""
+def _traffic(kernel_key, src_path, workload, field="hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per call) from the committed rocprofv3 counter summary, if it was
+    taken on this workload and the kernel source has not changed since."""
     path = os.path.join(PROFILE_DIR, f"{kernel_key}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -48,7 +49,7 @@ def _traffic(kernel_key, src_path, workload):
         return None
     if rec.get("workload", "").split(" ")[0] != workload:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get(field)
 
 
 def run_ring_forward(w, steps, warmup):
@@ -102,15 +103,31 @@ def _stats(xs):
     return {"median": round(statistics.median(xs), 4), "min": round(min(xs), 4), "max": round(max(xs), 4)}
 
 
-def _cpu_model():
+def _cpu_info():
+    """The host CPU as lscpu reports it (model name, and the BIOS model name where it differs),
+    plus os.cpu_count()."""
+    import subprocess
+    info = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:  # pragma: no cover
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key in ("Model name", "BIOS Model name", "CPU family", "Model", "Thread(s) per core",
+                       "Core(s) per socket", "Socket(s)", "CPU max MHz") and val:
+                info[key] = val
+    except (OSError, subprocess.SubprocessError):  # pragma: no cover
         pass
-    return None
+    if "Model name" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        info["Model name"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:  # pragma: no cover
+            pass
+    return {"cpu_model": info.get("Model name"), "lscpu": info, "os_cpu_count": os.cpu_count()}
 
 
 def _event_ms(fn, reps):
@@ -202,130 +219,227 @@ def side_measurements(w, tensors, reps=5):
     return res
 
 
-def run_training(w, steps, warmup):
-    """Ring forward + ring backward (training step of attention), or S2 forward + backward."""
+def run_training(w, steps, warmup, tensors=None):
+    """Ring forward + ring backward (training step of attention), or S2 forward + backward.
+
+    Every library call is bracketed by HIP events on the working stream, so the per-call (per
+    ring step) times of the forward and of the backward are measured inside the timed region.
+    After it, on the same inputs: the backward as one call over all keys (one chunk), to show what
+    the ring split costs the backward."""
     import torch
 
-    import long_context_exact_blockattn_amd as ba
     from long_context_exact_blockattn_amd import _lib
     from workloads import chunk_bounds, chunk_order, make_inputs
 
     dev = torch.device("cuda:0")
-    q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
-    q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    if tensors is None:
+        q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed,
+                                  with_dout=True)
+        q, k, v, do = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    else:
+        q, k, v, do = tensors
     b, s, hq, d = q.shape
+    o = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
+    lse = torch.empty(b, hq, s, device=dev)
+    delta = torch.empty(b, hq, s, device=dev)
+    dq_acc = torch.empty(b, s, hq, d, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
     if w.s2_group is not None:
-        o = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
-        lse = torch.empty(b, hq, s, device=dev)
-        delta = torch.empty(b, hq, s, device=dev)
-        dq_acc = torch.empty(b, s, hq, d, device=dev)
-        dq = torch.empty_like(q)
-        dk = torch.empty_like(k)
-        dv = torch.empty_like(v)
+        order, n = None, 1
 
-        def fwd():
+        def fwd(ev=None):
+            if ev is not None:
+                ev[0].record()
             _lib.s2attn_fwd(q, k, v, o, lse, group=w.s2_group, shift_head0=w.s2_shift_head0)
+            if ev is not None:
+                ev[1].record()
 
-        def bwd():
+        def bwd(ev=None):
             dq_acc.zero_()
+            if ev is not None:
+                ev[0].record()
             _lib.s2attn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, group=w.s2_group,
                             shift_head0=w.s2_shift_head0, dq_final=dq,
                             flags=_lib.BA_BWD_COMPUTE_DELTA | _lib.BA_BWD_FINALIZE_DQ)
-        order = None
+            if ev is not None:
+                ev[1].record()
     else:
         order = chunk_order(w.n_chunks, seed=w.seed)
         bounds = chunk_bounds(w.seqlen, w.n_chunks)
         o_acc = torch.empty(b, s, hq, d, device=dev)
-        lse = torch.empty(b, hq, s, device=dev)
-        o = torch.empty(b, s, hq, d, device=dev, dtype=torch.bfloat16)
-        delta = torch.empty(b, hq, s, device=dev)
-        dq_acc = torch.empty(b, s, hq, d, device=dev)
-        dq = torch.empty_like(q)
-        dk = torch.empty_like(k)
-        dv = torch.empty_like(v)
         n = len(order)
 
-        def fwd():
+        def fwd(ev=None):
             for t, c in enumerate(order):
                 c0, c1 = bounds[c]
+                if ev is not None:
+                    ev[t].record()
                 _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
                                    mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
                                    o_final=o if t == n - 1 else None, k_pos0=c0)
+            if ev is not None:
+                ev[n].record()
 
-        def bwd():
+        def bwd(ev=None):
             dq_acc.zero_()
             for t, c in enumerate(order):
                 c0, c1 = bounds[c]
                 flags = (_lib.BA_BWD_COMPUTE_DELTA if t == 0 else 0) | (_lib.BA_BWD_FINALIZE_DQ if t == n - 1 else 0)
+                if ev is not None:
+                    ev[t].record()
                 _lib.blockattn_bwd(q, k[:, c0:c1], v[:, c0:c1], o, do, lse, delta, dq_acc,
                                    dk[:, c0:c1], dv[:, c0:c1], dq_final=dq, flags=flags, k_pos0=c0)
+            if ev is not None:
+                ev[n].record()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evf = [mk() for _ in range(steps)]
+    evb = [mk() for _ in range(steps)]
     for _ in range(warmup):
         fwd(); bwd()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
+    for i in range(steps):
+        fwd(evf[i]); bwd(evb[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    fwd_ms = [e[0].elapsed_time(e[n]) for e in evf]
+    bwd_ms = [e[0].elapsed_time(e[n]) for e in evb]
+    fwd_call_ms = [e[t].elapsed_time(e[t + 1]) for e in evf for t in range(n)]
+    bwd_call_ms = [e[t].elapsed_time(e[t + 1]) for e in evb for t in range(n)]
     assert not torch.isnan(dq).any() and not torch.isnan(dk).any(), "NaN in gradients"
-    return {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "order": order}
+    res = {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "order": order, "calls_per_phase": n,
+           "fwd_call_ms": fwd_call_ms, "bwd_call_ms": bwd_call_ms}
+    if w.s2_group is None and n > 1:
+        def bwd_one_shot():
+            dq_acc.zero_()
+            _lib.blockattn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, dq_final=dq,
+                               flags=_lib.BA_BWD_COMPUTE_DELTA | _lib.BA_BWD_FINALIZE_DQ)
+        res["bwd_one_shot_ms"] = _event_ms(bwd_one_shot, 3)
+    return res
 
 
-def cpu_baseline(w, budget_heads=2, budget_flop=6e11, rows_budget_flop=1.5e11):
-    """The oracle as it stands, timed on a bounded sample of the same workload: the first query
-    heads with all ring steps (about 12 s of host work at the 32K headline shape; short sequences
-    in full), or, where two whole heads exceed the budget, the last query rows of head 0 (the rows
-    with the most allowed keys) against the whole sequence, in blocks of rows."""
+def _oracle_pool(fn, items):
+    """Run fn over items on a thread pool sized to the host's share of cores (at most 16, the CPU
+    share of one GPU on the boxes this runs on), with numpy's BLAS limited so that pool threads
+    times BLAS threads is that share; numpy releases the GIL inside its products and ufuncs.
+    Returns the number of cores used."""
+    from concurrent.futures import ThreadPoolExecutor
+    cores = max(1, min(16, os.cpu_count() or 1))
+    blas = 2 if cores >= 4 else 1
+    workers = max(1, cores // blas)
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=blas):
+            with ThreadPoolExecutor(max_workers=workers) as ex:
+                list(ex.map(fn, items))
+    else:  # pragma: no cover
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fn, items))
+    return workers * blas
+
+
+def cpu_baseline(w, budget_flop=1.2e12, rows_budget_flop=1.5e11):
+    """The oracle as it stands, timed on a bounded sample of the same workload: whole query heads
+    with all ring steps, one head per pool thread (about 10-20 s of host work at the 32K headline
+    shape; short sequences in full), or, where whole heads exceed the budget, the last query rows
+    of each head of a pool's worth (the rows with the most allowed keys) against the whole
+    sequence, in blocks of rows."""
     import numpy as np
 
     from oracle import ring_attention_forward, rows_forward
     from workloads import chunk_order, make_inputs
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
     print(f"timing the oracle on the host ({w.name}) ...", file=sys.stderr, flush=True)
     q, k, v = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed)
-    heads = list(range(w.heads_q if w.seqlen <= 4096 else min(budget_heads, w.heads_q)))
-    flop = w.fwd_flop() * len(heads) / w.heads_q
-    if flop <= budget_flop:
-        kv_heads = sorted({h // (w.heads_q // w.heads_kv) for h in heads})
-        qn = q[:, :, heads].float().numpy().astype(np.float64)
-        kn = k[:, :, kv_heads].float().numpy().astype(np.float64)
-        vn = v[:, :, kv_heads].float().numpy().astype(np.float64)
-        order = chunk_order(w.n_chunks, seed=w.seed)
+    pool = max(1, min(16, os.cpu_count() or 1)) // 2 or 1
+    per_head = w.fwd_flop() / w.heads_q
+    n_heads = w.heads_q if w.seqlen <= 4096 else max(1, min(w.heads_q, pool, int(budget_flop // per_head)))
+    grp = w.heads_q // w.heads_kv
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    if per_head * n_heads <= budget_flop:
+        heads = list(range(n_heads))
+        args = {}
+        for h in heads:
+            sl = lambda t, i: np.ascontiguousarray(t[:, :, i:i + 1].float().numpy().astype(np.float64))
+            args[h] = (sl(q, h), sl(k, h // grp), sl(v, h // grp))
+
+        def one(h):
+            ring_attention_forward(*args[h], order, w.chunk_len)
         t0 = time.perf_counter()
-        ring_attention_forward(qn, kn, vn, order, w.chunk_len)
+        cores = _oracle_pool(one, heads)
         dt = time.perf_counter() - t0
-        sample = (f"{w.name}: query heads 0-{len(heads) - 1} of {w.heads_q} at full S={w.seqlen}, all "
-                  f"{w.n_chunks} ring steps in the seeded order, numpy float64")
+        flop = per_head * n_heads
+        sample = (f"{w.name}: query heads 0-{n_heads - 1} of {w.heads_q} at full S={w.seqlen}, all "
+                  f"{w.n_chunks} ring steps in the seeded order, one head per thread, numpy float64")
     else:
         # causal: row i has i + 1 allowed keys; take rows from the end while the budget lasts
         S, per_key = w.seqlen, 4 * w.head_dim
-        n, flop = 0, 0
-        while n < S and flop + per_key * (S - n) <= rows_budget_flop:
-            flop += per_key * (S - n)
+        n, flop1 = 0, 0
+        while n < S and flop1 + per_key * (S - n) <= rows_budget_flop / pool:
+            flop1 += per_key * (S - n)
             n += 1
-        qn = q[:, :, :1].float().numpy()
-        kn = k[:, :, :1].float().numpy()
-        vn = v[:, :, :1].float().numpy()
+        heads = list(range(pool))
+        qn = q[:, :, :pool].float().numpy()
+        kn = k[:, :, : max(1, pool // grp)].float().numpy()
+        vn = v[:, :, : max(1, pool // grp)].float().numpy()
+        blocks = [(h, r0) for h in heads for r0 in range(S - n, S, 256)]
+
+        def one(item):
+            h, r0 = item
+            rows_forward(qn, kn, vn, 0, h, range(r0, min(r0 + 256, S)))
         t0 = time.perf_counter()
-        for r0 in range(S - n, S, 256):
-            rows_forward(qn, kn, vn, 0, 0, range(r0, min(r0 + 256, S)))
+        cores = _oracle_pool(one, blocks)
         dt = time.perf_counter() - t0
-        sample = (f"{w.name}: the last {n} query rows of head 0 of {w.heads_q} against all S={w.seqlen} keys "
-                  f"(a row's result is the same for any chunk order), numpy float64 in blocks of 256 rows")
+        flop = flop1 * pool
+        sample = (f"{w.name}: the last {n} query rows of heads 0-{pool - 1} of {w.heads_q} against all "
+                  f"S={w.seqlen} keys (a row's result is the same for any chunk order), numpy float64 in "
+                  f"blocks of 256 rows on a thread pool")
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{sample}; {dt:.1f} s for {flop:.3e} algorithmic flop",
             "seconds": round(dt, 3),
             "extrapolated_full_config_s": round(dt * w.fwd_flop() / flop, 1),
-            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+            **_cpu_info()}
+
+
+def cpu_baseline_backward(w, prefix=12288):
+    """The oracle's backward as it stands, on a bounded sample of a causal training workload: the
+    first `prefix` positions of query heads 0..n-1 (one head per pool thread).  A causal prefix is
+    a complete attention problem of its own (its rows see only its keys), so this is the same
+    computation at a shorter length; the rate is algorithmic flop (10 D per allowed pair) over
+    the wall time."""
+    import numpy as np
+
+    from oracle import attention_backward
+    from workloads import make_inputs
+
+    print(f"timing the oracle's backward on the host ({w.name}) ...", file=sys.stderr, flush=True)
+    pool = max(1, min(16, os.cpu_count() or 1)) // 2 or 1
+    n_heads = min(pool, w.heads_q)
+    q, k, v, do = make_inputs(w.batch, prefix, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
+    grp = w.heads_q // w.heads_kv
+    sl = lambda t, i: np.ascontiguousarray(t[:, :, i:i + 1].float().numpy().astype(np.float64))
+    args = {h: (sl(q, h), sl(k, h // grp), sl(v, h // grp), sl(do, h)) for h in range(n_heads)}
+
+    def one(h):
+        attention_backward(*args[h], row_block=512)
+    t0 = time.perf_counter()
+    cores = _oracle_pool(one, list(range(n_heads)))
+    dt = time.perf_counter() - t0
+    flop = 10.0 * w.head_dim * prefix * (prefix + 1) / 2 * n_heads
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{w.name} inputs drawn at S={prefix} (the seeded generator at the workload's head "
+                       f"counts), query heads 0-{n_heads - 1}: the oracle's full backward (forward "
+                       f"recompute, Delta, dQ, dK, dV) of that causal prefix, one head per thread, numpy "
+                       f"float64; {dt:.1f} s for {flop:.3e} algorithmic flop"),
+            "seconds": round(dt, 3),
+            "extrapolated_full_config_s": round(dt * w.bwd_flop() / flop, 1),
+            **_cpu_info()}
 
 
 def copy_calibration(reps):
@@ -438,49 +552,77 @@ def counter_summary(d, out=None, kernel=None):
         rec = {"kernel": "ba::fwd_kernel<128>", "workload": "llama2_7b_s32k_ring8",
                "kernel_source_sha": _src_sha(FWD_SRC), "dispatches": len(rows),
                "command": f"rocprofv3 --pmc {COUNTERS} -d {d} -o busy -- python -u bench.py --steps 1 "
-                          "--warmup 0 --no-cpu-baseline --no-side-measurements",
+                          "--warmup 0 --no-cpu-baseline --no-side-measurements --no-backward",
                **{k: round(v, 4) for k, v in avg.items()}}
         with open(out, "w") as f:
             json.dump(rec, f, indent=1)
 
 
-def traffic_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out):
-    """HBM bytes per forward launch from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled
-    by what the same counter reads for a plain copy of 1 GiB; written to the traffic summary that
-    bench.py reports while the kernel source is unchanged."""
-    kern = "fwd_kernel<128>"
-    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", kern)
-    write = _counter_per_dispatch(write_dir, "WRITE_SIZE", kern)
+TRAFFIC_TARGETS = {
+    # key: (kernels summed per launch / call, the launch kernel counted once per call, workload,
+    #       source file, bench arguments of the profiled run, summary file field)
+    "fwd": (("fwd_kernel<128>",), "fwd_kernel<128>", "llama2_7b_s32k_ring8", FWD_SRC,
+            "--steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements --no-backward",
+            "fwd_kernel_d128_traffic.json", "hbm_bytes_per_launch"),
+    "bwd": (("bwd_dkdv_kernel<128>", "bwd_dq_kernel<128>", "bwd_delta_kernel<128>"), "bwd_dq_kernel<128>",
+            "llama2_13b_s64k_ring8_train", BWD_SRC,
+            "--workload llama2_13b_s64k_ring8_train --steps 1 --warmup 0 --no-cpu-baseline",
+            "bwd_kernels_d128_traffic.json", "hbm_bytes_per_call"),
+}
+
+
+def traffic_summary(target, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per forward launch (target fwd) or per backward call (target bwd: the dK/dV, dQ
+    and, on the first call, delta launches of one blockattn_bwd call) from FETCH_SIZE /
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter reads for a plain
+    copy of 1 GiB; written to the traffic summary that bench.py reports while the kernel source
+    is unchanged."""
+    kernels, per_call_kernel, workload, src, bench_args, fname, field = TRAFFIC_TARGETS[target]
     cf = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "")
     cw = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "")
     n = 1 << 30
     # the copy launches dominate the calibration runs; take the largest dispatch (the 1 GiB copy)
     fscale = n / 1024.0 / max(cf)
     wscale = n / 1024.0 / max(cw)
-    fb = sum(fetch) / len(fetch) * 1024 * fscale
-    wb = sum(write) / len(write) * 1024 * wscale
+    calls = len(_counter_per_dispatch(fetch_dir, "FETCH_SIZE", per_call_kernel))
+    per_kernel = {}
+    fb = wb = 0.0
+    for kern in kernels:
+        fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", kern)
+        write = _counter_per_dispatch(write_dir, "WRITE_SIZE", kern)
+        if not fetch:
+            continue
+        f_tot = sum(fetch) * 1024 * fscale
+        w_tot = sum(write) * 1024 * wscale
+        per_kernel[kern] = {"dispatches": len(fetch),
+                            "fetch_size_kib_per_dispatch": [round(x, 1) for x in fetch],
+                            "write_size_kib_per_dispatch": [round(x, 1) for x in write],
+                            "hbm_fetch_bytes_per_dispatch": int(f_tot / len(fetch)),
+                            "hbm_write_bytes_per_dispatch": int(w_tot / max(len(write), 1))}
+        fb += f_tot
+        wb += w_tot
+    cmd = lambda c, d, o: f"rocprofv3 --pmc {c} -d {d} -o {o} -- python -u bench.py {bench_args}"
     rec = {
-        "kernel": "ba::fwd_kernel<128>",
-        "workload": "llama2_7b_s32k_ring8 (8 ring steps, one dispatch each)",
-        "kernel_source_sha": _src_sha(FWD_SRC),
+        "kernel": " + ".join(f"ba::{k}" for k in kernels),
+        "workload": f"{workload} ({calls} calls, one per ring step)",
+        "kernel_source_sha": _src_sha(src),
         "commands": [
-            f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o fetch -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
-            f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o write -- python -u bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
+            cmd("FETCH_SIZE", fetch_dir, "fetch"), cmd("WRITE_SIZE", write_dir, "write"),
             f"rocprofv3 --pmc FETCH_SIZE -d {copy_fetch_dir} -o cfetch -- python -u bench.py --copy-calibration --steps 3",
             f"rocprofv3 --pmc WRITE_SIZE -d {copy_write_dir} -o cwrite -- python -u bench.py --copy-calibration --steps 3",
-            f"python bench.py --traffic-summary {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}",
+            f"python bench.py --traffic-summary {target} {fetch_dir} {write_dir} {copy_fetch_dir} {copy_write_dir}",
         ],
         "copy_calibration": {"bytes_per_copy": n, "fetch_size_kib": max(cf), "write_size_kib": max(cw),
                              "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
-        "fetch_size_kib_per_dispatch": [round(x, 1) for x in fetch],
-        "write_size_kib_per_dispatch": [round(x, 1) for x in write],
-        "hbm_bytes_per_launch": int(fb + wb),
-        "hbm_fetch_bytes_per_launch": int(fb),
-        "hbm_write_bytes_per_launch": int(wb),
+        "per_kernel": per_kernel,
+        field: int((fb + wb) / calls),
+        field.replace("hbm_", "hbm_fetch_"): int(fb / calls),
+        field.replace("hbm_", "hbm_write_"): int(wb / calls),
     }
+    out = os.path.join(PROFILE_DIR, fname)
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps({"hbm_bytes_per_launch": rec["hbm_bytes_per_launch"], "out": out}))
+    print(json.dumps({field: rec[field], "out": out}))
 
 
 def ffn_cpu_baseline(w, sample_rows=32768):
@@ -553,30 +695,86 @@ def ffn_line(w, args):
     print(json.dumps(line), flush=True)
 
 
+def bwd_algorithmic_bytes(w):
+    """HBM bytes the ring backward must move, per blockattn_bwd call (averaged over the ring's
+    calls): for chunk c the rows at or after the chunk's start read Q and dO (bf16), LSE and delta
+    (fp32), and read and write their fp32 dQ accumulator; the chunk's K and V are read and its dK,
+    dV (bf16) written; the first call also reads O and dO and writes delta, the last writes bf16 dQ.
+    Causal, one query block holding every row (query position = row)."""
+    hq, hkv, d, S, n = w.heads_q, w.heads_kv, w.head_dim, w.seqlen, w.n_chunks
+    C = w.chunk_len
+    tot = 0
+    for c in range(n):
+        rows = max(0, S - c * C)
+        ck = min(C, S - c * C)
+        tot += rows * hq * (d * (2 + 2) + 4 * 2 + d * 4 * 2) + ck * hkv * d * 2 * 4
+    tot += S * hq * (d * 2 * 2 + 4) + S * hq * d * 2
+    return tot / n
+
+
+def training_record(w, steps, warmup, cpu=True, tensors=None):
+    """Forward + backward of a training workload: phase times and rates, the backward's roofline
+    per blockattn_bwd call (one ring step: its dK/dV and dQ launches, plus the delta launch on the
+    first step), the backward as one call against the ring, and the oracle's backward on a bounded
+    sample as the CPU baseline."""
+    import statistics
+    r = run_training(w, steps, warmup, tensors=tensors)
+    ms = r["wall_s"] * 1e3 / steps
+    fwd_med, bwd_med = statistics.median(r["fwd_ms"]), statistics.median(r["bwd_ms"])
+    n = r["calls_per_phase"]
+    call_ms = sum(r["bwd_call_ms"]) / len(r["bwd_call_ms"])
+    achieved = w.bwd_flop() / n / (call_ms * 1e-3) / 1e12
+    traffic = _traffic("bwd_kernels_d128", BWD_SRC, w.name, field="hbm_bytes_per_call")
+    rec = {
+        "workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+        "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks, "s2_group": w.s2_group,
+        "chunk_order": r["order"], "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "step_tflops": round((w.fwd_flop() + w.bwd_flop()) / (ms * 1e-3) / 1e12, 2),
+        # medians of per-step HIP-event times of each phase
+        "fwd_ms": round(fwd_med, 4), "bwd_ms": round(bwd_med, 4),
+        "fwd_tflops": round(w.fwd_flop() / fwd_med / 1e9, 2),
+        "bwd_tflops": round(w.bwd_flop() / bwd_med / 1e9, 2),
+        "bwd_pct_bf16_peak": round(100 * w.bwd_flop() / bwd_med / 1e9 / PEAK_BF16_TFLOPS, 2),
+        "step_ms": {"fwd": _stats(r["fwd_ms"]), "bwd": _stats(r["bwd_ms"])},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": (f"bwd_dkdv_kernel<{w.head_dim}> + bwd_dq_kernel<{w.head_dim}> (one blockattn_bwd "
+                                f"call per ring step; bwd_delta_kernel<{w.head_dim}> on the first)"),
+                     "avg_launch_ms": round(call_ms, 4), "launches_per_step": n,
+                     "algorithmic_bytes_per_launch": int(bwd_algorithmic_bytes(w)) if w.s2_group is None else None},
+    }
+    if "bwd_one_shot_ms" in r:
+        one = r["bwd_one_shot_ms"]
+        rec["bwd_one_shot"] = {"ms": round(one, 4), "tflops": round(w.bwd_flop() / one / 1e9, 2),
+                               "ring_overhead_pct": round(100 * (bwd_med / one - 1), 2)}
+    if cpu:
+        rec["cpu_baseline"] = cpu_baseline_backward(w)
+    return rec
+
+
 def training_line(w, args):
     """One JSON line for a forward+backward workload (attention training step)."""
-    import statistics
-    r = run_training(w, args.steps, args.warmup)
-    ms = r["wall_s"] * 1e3 / args.steps
-    fwd_med, bwd_med = statistics.median(r["fwd_ms"]), statistics.median(r["bwd_ms"])
-    flop = w.fwd_flop() + w.bwd_flop()
-    tflops = flop / (ms * 1e-3) / 1e12
+    rec = training_record(w, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
+    tflops = rec["step_tflops"]
     line = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
-                   "seq_len": w.seqlen, "head_dim": w.head_dim, "ring_chunks": w.n_chunks,
-                   "s2_group": w.s2_group, "chunk_order": r["order"], "phases": "forward+backward",
-                   "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                   # medians of per-step HIP-event times of each phase
-                   "fwd_ms": round(fwd_med, 4), "bwd_ms": round(bwd_med, 4),
-                   "fwd_tflops": round(w.fwd_flop() / fwd_med / 1e9, 2),
-                   "bwd_tflops": round(w.bwd_flop() / bwd_med / 1e9, 2)},
-        "step_ms": {"fwd": _stats(r["fwd_ms"]), "bwd": _stats(r["bwd_ms"])},
+        "config": {k: rec[k] for k in ("workload", "batch", "heads_q", "heads_kv", "seq_len", "head_dim",
+                                       "ring_chunks", "s2_group", "chunk_order", "fwd_ms", "bwd_ms",
+                                       "fwd_tflops", "bwd_tflops")},
+        "roofline": rec["roofline"],
+        "step_ms": rec["step_ms"],
         "peak_basis": PEAK_BASIS,
     }
+    line["config"]["phases"] = "forward+backward"
+    line["config"]["pct_bf16_peak"] = round(100 * tflops / PEAK_BF16_TFLOPS, 2)
+    if "bwd_one_shot" in rec:
+        line["bwd_one_shot"] = rec["bwd_one_shot"]
+    if "cpu_baseline" in rec:
+        line["cpu_baseline"] = rec["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 
@@ -598,8 +796,11 @@ def main():
                     help="with --counter-summary: summarise this kernel instead of the forward (printed only)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel statistics of a rocprofv3 --kernel-trace output directory")
-    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="write the forward kernel's HBM traffic summary from four rocprofv3 --pmc runs")
+    ap.add_argument("--traffic-summary", nargs=5, metavar=("TARGET", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the HBM traffic summary of TARGET (fwd: the forward kernel; bwd: one backward "
+                         "call's kernels) from four rocprofv3 --pmc runs")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training workload's backward record of the default line")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
@@ -611,7 +812,9 @@ def main():
         trace_summary(args.trace_summary)
         return
     if args.traffic_summary:
-        traffic_summary(*args.traffic_summary, os.path.join(PROFILE_DIR, "fwd_kernel_d128_traffic.json"))
+        if args.traffic_summary[0] not in TRAFFIC_TARGETS:
+            ap.error(f"--traffic-summary TARGET must be one of {sorted(TRAFFIC_TARGETS)}")
+        traffic_summary(*args.traffic_summary)
         return
     if args.copy_calibration:
         copy_calibration(args.steps)
@@ -666,6 +869,15 @@ def main():
             line["ring_staged"] = side["ring_staged"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
+    if not args.no_backward:
+        # the backward half of the metric: the training step at the Llama-2-13B shape, its own
+        # roofline and its own oracle baseline
+        import torch
+        del tensors, r
+        torch.cuda.empty_cache()
+        wb = get("llama2_13b_s64k_ring8_train")
+        print(f"backward record ({wb.name}) ...", file=sys.stderr, flush=True)
+        line["backward"] = training_record(wb, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 

@@ -24,9 +24,12 @@
  *  - Layouts: query-shaped tensors (q, o, o_final, dout, dq_acc, dq_final) are
  *    [B, Sq, Hq, D]; key-shaped tensors (k, v, dk, dv) are [B, Sk, Hkv, D].  The
  *    D axis is contiguous (stride 1); the b, s, h strides are given in ELEMENTS
- *    in ba_desc (q_stride for every query-shaped tensor, kv_stride for every
- *    key-shaped one) and must be non-negative multiples of 8.  Row statistics
- *    (lse, delta) are dense fp32 [B, Hq, Sq].
+ *    in ba_desc and must be non-negative multiples of 8: q_stride for q,
+ *    o_stride for every other query-shaped tensor (o, o_final, dout, dq_acc,
+ *    dq_final; in lse_merge o_acc, o_part, o_final), kv_stride for every
+ *    key-shaped one.  So q may be a strided view (say a slice of a packed
+ *    [B, S, 3, H, D] projection) while the outputs are dense, or the reverse.
+ *    Row statistics (lse, delta) are dense fp32 [B, Hq, Sq].
  *  - Pointers to bf16/fp32 tensors must be 16-byte aligned; lse/delta 4-byte.
  *  - Dtypes: q, k, v, dout are bf16.  LSE, delta and accumulators are fp32.
  *    Every bf16 store rounds to nearest even.
@@ -85,8 +88,10 @@ typedef struct {
   int32_t causal;     /* 1: causal mask on global positions; 0: every key allowed */
   float scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim); the forward and backward
                          return BA_ERR_SHAPE for NaN or inf */
-  int64_t q_stride[3];  /* (b, s, h) element strides of every query-shaped tensor */
-  int64_t kv_stride[3]; /* (b, s, h) element strides of every key-shaped tensor */
+  int64_t q_stride[3];  /* (b, s, h) element strides of q */
+  int64_t kv_stride[3]; /* (b, s, h) element strides of every key-shaped tensor (k, v, dk, dv) */
+  int64_t o_stride[3];  /* (b, s, h) element strides of every other query-shaped tensor
+                           (o, o_final, dout, dq_acc, dq_final; lse_merge: all of its tensors) */
 } ba_desc;
 
 /* S2-Attn layout (LongLoRA summary, Summary: tokens split into groups, attention
@@ -125,8 +130,9 @@ int blockattn_fwd(const ba_desc* desc, const void* q, const void* k, const void*
  *   L = log(e^La + e^Lb),  O = e^(La - L) O_a + e^(Lb - L) O_b,
  * a pair with LSE = -inf contributing nothing whatever its O holds, and two
  * such pairs giving (0, -inf).  Uses batch, heads_q, head_dim, seqlen_q and
- * q_stride of desc.  o_acc is fp32; o_part is fp32 or bf16 (part_dtype);
- * o_final (nullable) receives bf16 of the merged output.  Same source as
+ * o_stride of desc (shared by o_acc, o_part and o_final).  o_acc is fp32;
+ * o_part is fp32 or bf16 (part_dtype); o_final (nullable) receives bf16 of the
+ * merged output.  Same source as
  * blockattn_fwd (order-independent combination of blocks). */
 int lse_merge(const ba_desc* desc, float* o_acc, float* lse_acc, const void* o_part,
               int32_t part_dtype, const float* lse_part, void* o_final, hipStream_t stream);

@@ -39,6 +39,7 @@ class BaDesc(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("q_stride", ctypes.c_int64 * 3),
         ("kv_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -149,10 +150,11 @@ def _bshd_strides(t, name):
     return (t.stride(0), t.stride(1), t.stride(2))
 
 
-def _same_layout(ref, t, name, shape=None, ref_name="q"):
-    """t has ref's shape and, on every axis longer than one, ref's stride: the kernels address
-    every query-shaped tensor with q's strides, and an axis of length one is never stepped along
-    (torch keeps arbitrary strides there, e.g. after .contiguous() of a slice of a batch of one)."""
+def _same_layout(ref, t, name, shape=None, ref_name="o"):
+    """t has ref's shape and, on every axis longer than one, ref's stride: the kernels address the
+    tensors of one stride group (q; k, v, dk, dv; o, o_final, dout, dq_acc, dq_final) with one set
+    of strides, and an axis of length one is never stepped along (torch keeps arbitrary strides
+    there, e.g. after .contiguous() of a slice of a batch of one)."""
     if t is None:
         return
     if tuple(t.shape) != tuple(ref.shape if shape is None else shape):
@@ -170,10 +172,14 @@ def _stats_ok(t, shape, name):
         raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {tuple(shape)}")
 
 
-def make_desc(q, k, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
+def make_desc(q, k, o=None, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
+    """Descriptor of a call: shapes from q and k, strides from q (q_stride), k (kv_stride) and
+    o (o_stride: every other query-shaped tensor; q's own strides when o is None)."""
     if q.dim() != 4 or (k is not None and k.dim() != 4):
         raise ValueError("q and k must be [B, S, H, D]")
     b, sq, hq, d = q.shape
+    if o is not None and tuple(o.shape) != tuple(q.shape):
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {tuple(q.shape)}")
     # the descriptor carries one batch size and one head size for every tensor of the call
     if k is not None and (k.shape[0] != b or k.shape[3] != d):
         raise ValueError(f"k {tuple(k.shape)} must have q's batch ({b}) and head_dim ({d})")
@@ -186,6 +192,7 @@ def make_desc(q, k, *, q_pos0=0, k_pos0=0, causal=True, scale=None):
     desc.scale = 0.0 if scale is None else float(scale)
     desc.q_stride[:] = _used_strides(q, "q")
     desc.kv_stride[:] = _used_strides(k, "k") if k is not None else (0, 0, 0)
+    desc.o_stride[:] = _used_strides(q if o is None else o, "o")
     return desc
 
 
@@ -211,10 +218,9 @@ def blockattn_fwd(q, k, v, o, lse, *, mode=BA_OVERWRITE, o_final=None, q_pos0=0,
     """One ring step; see blockattn_fwd in include/blockattn.h."""
     _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
                  (lse, "lse", "float32"), (o_final, "o_final", "bfloat16")])
-    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+    desc = make_desc(q, k, o, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
     _same_layout(k, v, "v", ref_name="k")
-    _same_layout(q, o, "o")
-    _same_layout(q, o_final, "o_final")
+    _same_layout(o, o_final, "o_final")
     _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
     st = load().blockattn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                               _dtype_code(o, "o"), _ptr(lse), int(mode), _ptr(o_final), _stream(stream))
@@ -225,9 +231,9 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, *, o_final=None, stream=None):
     """(o_acc, lse_acc) := merge with (o_part, lse_part); see lse_merge in include/blockattn.h."""
     _require(o_acc, [(o_acc, "o_acc", "float32"), (lse_acc, "lse_acc", "float32"), (o_part, "o_part", None),
                      (lse_part, "lse_part", "float32"), (o_final, "o_final", "bfloat16")])
-    desc = make_desc(o_acc, None)
-    _same_layout(o_acc, o_part, "o_part")
-    _same_layout(o_acc, o_final, "o_final")
+    desc = make_desc(o_acc, None, o_acc)
+    _same_layout(o_acc, o_part, "o_part", ref_name="o_acc")
+    _same_layout(o_acc, o_final, "o_final", ref_name="o_acc")
     shape = (o_acc.shape[0], o_acc.shape[2], o_acc.shape[1])
     _stats_ok(lse_acc, shape, "lse_acc")
     _stats_ok(lse_part, shape, "lse_part")
@@ -239,9 +245,8 @@ def lse_merge(o_acc, lse_acc, o_part, lse_part, *, o_final=None, stream=None):
 def s2attn_fwd(q, k, v, o, lse, *, group, shift_head0, scale=None, stream=None):
     _require(q, [(q, "q", "bfloat16"), (k, "k", "bfloat16"), (v, "v", "bfloat16"), (o, "o", None),
                  (lse, "lse", "float32")])
-    desc = make_desc(q, k, causal=True, scale=scale)
+    desc = make_desc(q, k, o, causal=True, scale=scale)
     _same_layout(k, v, "v", ref_name="k")
-    _same_layout(q, o, "o")
     _stats_ok(lse, (q.shape[0], q.shape[2], q.shape[1]), "lse")
     s2 = BaS2Desc(int(group), int(shift_head0))
     st = load().s2attn_fwd(ctypes.byref(desc), ctypes.byref(s2), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
@@ -254,8 +259,10 @@ def _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final):
                  (dout, "dout", "bfloat16"), (lse, "lse", "float32"), (delta, "delta", "float32"),
                  (dq_acc, "dq_acc", "float32"), (dk, "dk", None), (dv, "dv", None),
                  (dq_final, "dq_final", "bfloat16")])
-    for t, n in ((o, "o"), (dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
-        _same_layout(q, t, n)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {tuple(q.shape)}")
+    for t, n in ((dout, "dout"), (dq_acc, "dq_acc"), (dq_final, "dq_final")):
+        _same_layout(o, t, n)
     for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
         _same_layout(k, t, n, ref_name="k")
     if dk.dtype != dv.dtype:
@@ -269,7 +276,7 @@ def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None
                   q_pos0=0, k_pos0=0, causal=True, scale=None, stream=None):
     """One ring step of the backward; see blockattn_bwd in include/blockattn.h."""
     _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final)
-    desc = make_desc(q, k, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+    desc = make_desc(q, k, o, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
     st = load().blockattn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                               _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
                               _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
@@ -279,7 +286,7 @@ def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None
 def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_head0, dq_final=None,
                flags=0, scale=None, stream=None):
     _check_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dq_final)
-    desc = make_desc(q, k, causal=True, scale=scale)
+    desc = make_desc(q, k, o, causal=True, scale=scale)
     s2 = BaS2Desc(int(group), int(shift_head0))
     st = load().s2attn_bwd(ctypes.byref(desc), ctypes.byref(s2), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                            _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),

@@ -108,6 +108,7 @@ int main() {
   const int64_t strides[3] = {S * H * D, H * D, D};
   memcpy(d.q_stride, strides, sizeof strides);
   memcpy(d.kv_stride, strides, sizeof strides);
+  memcpy(d.o_stride, strides, sizeof strides);
 
   // ---- 1. validation: nothing is enqueued on an error
   {
@@ -125,6 +126,10 @@ int main() {
     bad.q_stride[1] = H * D + 4;
     if (blockattn_fwd(&bad, q, k, v, o_one, BA_F32, lse_one, BA_OVERWRITE, nullptr, st) != BA_ERR_STRIDE)
       return fail("stride not a multiple of 8 not rejected");
+    bad = d;
+    bad.o_stride[2] = -D;
+    if (blockattn_fwd(&bad, q, k, v, o_one, BA_F32, lse_one, BA_OVERWRITE, nullptr, st) != BA_ERR_STRIDE)
+      return fail("negative output stride not rejected");
     HIP_OK(hipStreamSynchronize(st));
     std::vector<float> zero(n);
     HIP_OK(hipMemcpy(zero.data(), o_one, n * 4, hipMemcpyDeviceToHost));

@@ -37,8 +37,9 @@ struct BwdArgs {
   void* dk;
   void* dv;
   bf16* dq_final;
-  int64_t qs_b, qs_s, qs_h;
-  int64_t ks_b, ks_s, ks_h;
+  int64_t qs_b, qs_s, qs_h;  // element strides of q
+  int64_t ks_b, ks_s, ks_h;  // element strides of k, v, dk, dv
+  int64_t os_b, os_s, os_h;  // element strides of o, dout, dq_acc, dq_final
   int64_t Sq, Sk, q_pos0, k_pos0;
   int32_t B, Hq, Hkv, grp;
   int32_t causal, s2_group, s2_shift_head0;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a, int64_t n_thr
     h = (int)(rowid % a.Hq);
     s = (rowid / a.Hq) % a.Sq;
     b = rowid / ((int64_t)a.Hq * a.Sq);
-    const int64_t off = b * a.qs_b + s * a.qs_s + (int64_t)h * a.qs_h + 8 * c;
+    const int64_t off = b * a.os_b + s * a.os_s + (int64_t)h * a.os_h + 8 * c;
     const bf16x8 x = *(const bf16x8*)(a.dout + off);
     const bf16x8 y = *(const bf16x8*)(a.o + off);
 #pragma unroll
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int64_t wave_cmax = wave_cmin + 31;
   const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
   const int64_t qoff = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h;
+  const int64_t ooff = (int64_t)b * a.os_b + row * a.os_s + (int64_t)h * a.os_h;
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       qf[kk] = row_ok ? *(const bf16x8*)(a.q + qoff + 16 * kk + 8 * hl) : bf16x8{};
-      df[kk] = row_ok ? *(const bf16x8*)(a.dout + qoff + 16 * kk + 8 * hl) : bf16x8{};
+      df[kk] = row_ok ? *(const bf16x8*)(a.dout + ooff + 16 * kk + 8 * hl) : bf16x8{};
     }
     // per-lane LDS offsets: direct reads (row l32, chunk 2kk+hl) and transposed reads
     int n_off[KK];
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   if (!row_ok) return;
-  const int64_t obase = qoff + 4 * hl;
+  const int64_t obase = ooff + 4 * hl;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -406,6 +408,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     TileLoader<D, BM, kKvThreads> ld;
     ld.init(wave, lane);
     const int qs_s = (int)a.qs_s;
+    const int os_s = (int)a.os_s;
     // tiles run over the group's heads, each over the query tiles [qt_begin, qt_end); the
     // loads and the compute each keep their own position (no divisions per tile)
     struct Pos {
@@ -433,9 +436,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         st_l = a.lse[li];
         st_d = a.delta[li];
       }
-      const int64_t base = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
-      ld.issue(a.q + base, qs_s, (int)t.rows, qd, wave);
-      ld.issue(a.dout + base, qs_s, (int)t.rows, qd + TILE, wave);
+      const int64_t qbase = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
+      const int64_t obase = (int64_t)b * a.os_b + t.row0 * a.os_s + (int64_t)hh * a.os_h;
+      ld.issue(a.q + qbase, qs_s, (int)t.rows, qd, wave);
+      ld.issue(a.dout + obase, os_s, (int)t.rows, qd + TILE, wave);
     };
     auto put_stats = [&](int buf) {
       if (tid < BM) {

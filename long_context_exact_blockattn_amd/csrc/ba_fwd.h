@@ -31,8 +31,9 @@ struct FwdArgs {
   void* o;          // fp32 or bf16 [B,Sq,Hq,D]
   float* lse;       // [B,Hq,Sq]
   bf16* o_final;    // nullable bf16 [B,Sq,Hq,D]
-  int64_t qs_b, qs_s, qs_h;  // element strides of query-shaped tensors
-  int64_t ks_b, ks_s, ks_h;  // element strides of key-shaped tensors
+  int64_t qs_b, qs_s, qs_h;  // element strides of q
+  int64_t ks_b, ks_s, ks_h;  // element strides of k and v
+  int64_t os_b, os_s, os_h;  // element strides of o and o_final
   int64_t Sq, Sk, q_pos0, k_pos0;
   int32_t B, Hq, Hkv, grp;
   int32_t causal, accumulate, o_f32;
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
     if (!row_ok[qb]) continue;
     const int64_t row = qt.row0 + rloc[qb];
     const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
-    const int64_t obase = (int64_t)b * a.qs_b + row * a.qs_s + (int64_t)h * a.qs_h + 4 * hl;
+    const int64_t obase = (int64_t)b * a.os_b + row * a.os_s + (int64_t)h * a.os_h + 4 * hl;
     float ca = 0.f, cc = inv_l, L2 = lse2_c;
     if (a.accumulate) {
       const float la2 = a.lse[lse_idx] * kLog2e;

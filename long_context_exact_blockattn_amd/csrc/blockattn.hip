@@ -39,7 +39,8 @@ int check_desc(const ba_desc* d) {
   if (d->causal != 0 && d->causal != 1) return BA_ERR_SHAPE;
   int r = check_strides(d->q_stride);
   if (r) return r;
-  return check_strides(d->kv_stride);
+  if ((r = check_strides(d->kv_stride))) return r;
+  return check_strides(d->o_stride);
 }
 
 int check_s2(const ba_desc* d, const ba_s2_desc* s2) {
@@ -92,6 +93,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.o = o; a.lse = lse; a.o_final = (bf16*)o_final;
   a.qs_b = d->q_stride[0]; a.qs_s = d->q_stride[1]; a.qs_h = d->q_stride[2];
   a.ks_b = d->kv_stride[0]; a.ks_s = d->kv_stride[1]; a.ks_h = d->kv_stride[2];
+  a.os_b = d->o_stride[0]; a.os_s = d->o_stride[1]; a.os_h = d->o_stride[2];
   a.Sq = d->seqlen_q; a.Sk = d->seqlen_k; a.q_pos0 = d->q_pos0; a.k_pos0 = d->k_pos0;
   a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.grp = d->heads_q / d->heads_kv;
   a.causal = s2 ? 1 : d->causal;
@@ -118,7 +120,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
     StoreArgs st;
     st.o_acc = (const float*)o;
     st.o_final = (bf16*)o_final;
-    st.s_b = d->q_stride[0]; st.s_s = d->q_stride[1]; st.s_h = d->q_stride[2];
+    st.s_b = d->o_stride[0]; st.s_s = d->o_stride[1]; st.s_h = d->o_stride[2];
     st.rows = skip_qt * kFwdBM;
     st.Hq = d->heads_q; st.D = d->head_dim;
     st.n_threads = (int64_t)d->batch * st.rows * d->heads_q * (d->head_dim / 8);
@@ -162,6 +164,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.dq_final = (bf16*)dq_final;
   a.qs_b = d->q_stride[0]; a.qs_s = d->q_stride[1]; a.qs_h = d->q_stride[2];
   a.ks_b = d->kv_stride[0]; a.ks_s = d->kv_stride[1]; a.ks_h = d->kv_stride[2];
+  a.os_b = d->o_stride[0]; a.os_s = d->o_stride[1]; a.os_h = d->o_stride[2];
   a.Sq = d->seqlen_q; a.Sk = d->seqlen_k; a.q_pos0 = d->q_pos0; a.k_pos0 = d->k_pos0;
   a.B = d->batch; a.Hq = d->heads_q; a.Hkv = d->heads_kv; a.grp = d->heads_q / d->heads_kv;
   a.causal = s2 ? 1 : d->causal;
@@ -284,7 +287,7 @@ int lse_merge(const ba_desc* d, float* o_acc, float* lse_acc, const void* o_part
   MergeArgs a;
   a.o_acc = o_acc; a.lse_acc = lse_acc; a.o_part = o_part; a.lse_part = lse_part;
   a.o_final = (bf16*)o_final;
-  a.s_b = d->q_stride[0]; a.s_s = d->q_stride[1]; a.s_h = d->q_stride[2];
+  a.s_b = d->o_stride[0]; a.s_s = d->o_stride[1]; a.s_h = d->o_stride[2];
   a.Sq = d->seqlen_q; a.Hq = d->heads_q; a.D = d->head_dim; a.part_f32 = part_dtype == BA_F32;
   a.n_threads = (int64_t)d->batch * d->seqlen_q * d->heads_q * (d->head_dim / 8);
   const int64_t blocks = ceil_div(a.n_threads, 256);

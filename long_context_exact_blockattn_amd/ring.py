@@ -116,13 +116,23 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
     return out, lse, o_acc
 
 
+def _empty_in_layout(t, dtype):
+    """An uninitialised tensor with t's shape and element strides (dense when t is): gradients of
+    key-shaped tensors share k's strides in the C ABI.  A strided t (say a slice of a packed
+    projection) gets storage spanning its strides, gaps included."""
+    if t.is_contiguous():
+        return torch.empty(t.shape, device=t.device, dtype=dtype)
+    return torch.empty_strided(t.shape, t.stride(), device=t.device, dtype=dtype)
+
+
 def ring_backward(q, k, v, o, dout, lse, n_chunks, order=None, *, causal=True, scale=None,
-                  dkv_dtype=torch.bfloat16, stream=None):
+                  dkv_dtype=torch.bfloat16, dk=None, dv=None, stream=None):
     """Backward over key/value chunks: returns (dq bf16, dk, dv).
 
     The first step also computes delta = rowsum(dout * o); every step writes
     its chunk's dK, dV and adds into the fp32 dQ accumulator; the last step
-    converts dQ to bf16.
+    converts dQ to bf16.  dq and the fp32 accumulator take o's layout; dk and dv
+    (allocated in k's layout unless given) must share k's strides.
     """
     bounds = _bounds(k.shape[1], n_chunks)
     order = list(range(len(bounds))) if order is None else list(order)
@@ -130,10 +140,10 @@ def ring_backward(q, k, v, o, dout, lse, n_chunks, order=None, *, causal=True, s
         raise ValueError("order must be a permutation of the chunk indices")
     b, s, hq, d = q.shape
     delta = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
-    dq_acc = torch.zeros(b, s, hq, d, device=q.device, dtype=torch.float32)
-    dq = torch.empty(b, s, hq, d, device=q.device, dtype=torch.bfloat16)
-    dk = torch.empty(k.shape, device=k.device, dtype=dkv_dtype)
-    dv = torch.empty(v.shape, device=v.device, dtype=dkv_dtype)
+    dq_acc = _empty_in_layout(o, torch.float32).zero_()
+    dq = _empty_in_layout(o, torch.bfloat16)
+    dk = _empty_in_layout(k, dkv_dtype) if dk is None else dk
+    dv = _empty_in_layout(k, dkv_dtype) if dv is None else dv
     for t, c in enumerate(order):
         c0, c1 = bounds[c]
         flags = 0

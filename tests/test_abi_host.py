@@ -41,6 +41,7 @@ def _desc(**kw):
     hq, hkv, D = d.heads_q, d.heads_kv, d.head_dim
     d.q_stride[:] = kw.get("qs", (d.seqlen_q * hq * D, hq * D, D))
     d.kv_stride[:] = kw.get("ks", (d.seqlen_k * hkv * D, hkv * D, D))
+    d.o_stride[:] = kw.get("os", (d.seqlen_q * hq * D, hq * D, D))
     return d
 
 
@@ -62,6 +63,9 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, _desc(ks=(0, -8, 8))) == _lib.BA_ERR_STRIDE
     assert _fwd(lib, _desc(ks=(0, 1 << 24, 8))) == _lib.BA_ERR_STRIDE  # 32-bit tile offsets
     assert _fwd(lib, _desc(qs=(0, 1 << 24, 8))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(os=(0, 260, 8))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(os=(-8, 256, 8))) == _lib.BA_ERR_STRIDE
+    assert _fwd(lib, _desc(os=(0, 1 << 24, 8))) == _lib.BA_ERR_STRIDE
     assert _fwd(lib, _desc(), q=FAKE + 2) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), lse=FAKE + 2) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), of=FAKE + 8) == _lib.BA_ERR_ALIGN
@@ -272,17 +276,17 @@ def test_unreached_causal_tiles_are_the_last_ranks(lib, Sq, Sk, q0, k0):
 
 
 def test_binding_layout_check_ignores_length_one_axes():
-    """The kernels address every query-shaped tensor with q's strides; an axis of length one is
-    never stepped along, so its stride may differ (torch keeps a slice's batch stride in
-    .contiguous() of a batch of one), while a real stride mismatch is refused."""
+    """The kernels address the tensors of one stride group with one set of strides; an axis of
+    length one is never stepped along, so its stride may differ (torch keeps a slice's batch
+    stride in .contiguous() of a batch of one), while a real stride mismatch is refused."""
     import torch
-    q = torch.zeros(1, 1000, 4, 128)[:, 300:700].contiguous()
-    o = torch.zeros(1, 400, 4, 128)
-    assert q.stride(0) != o.stride(0)
-    _lib._same_layout(q, o, "o")
-    q2 = torch.zeros(2, 1000, 4, 128)[:, 300:700]
-    with pytest.raises(ValueError, match="strides as q"):
-        _lib._same_layout(q2, torch.zeros(2, 400, 4, 128), "o")
+    o = torch.zeros(1, 1000, 4, 128)[:, 300:700].contiguous()
+    dout = torch.zeros(1, 400, 4, 128)
+    assert o.stride(0) != dout.stride(0)
+    _lib._same_layout(o, dout, "dout")
+    o2 = torch.zeros(2, 1000, 4, 128)[:, 300:700]
+    with pytest.raises(ValueError, match="strides as o"):
+        _lib._same_layout(o2, torch.zeros(2, 400, 4, 128), "dout")
     k = torch.zeros(2, 64, 1, 128)
     v = torch.zeros(2, 64, 3, 128)[:, :, 1:2]  # sequence stride 384 against k's 128
     with pytest.raises(ValueError, match="strides as k"):
@@ -299,6 +303,7 @@ def test_descriptor_zeroes_strides_of_length_one_axes(lib):
     x = torch.zeros(1, 300, 2, 128).as_strided((1, 300, 2, 128), (12345, 256, 128, 1))
     d = _lib.make_desc(x, x)
     assert tuple(d.q_stride) == (0, 256, 128) and tuple(d.kv_stride) == (0, 256, 128)
+    assert tuple(d.o_stride) == (0, 256, 128)
     # validation passes the strides and stops at the (fake) misaligned pointer instead
     assert _fwd(lib, d, q=FAKE + 2) == _lib.BA_ERR_ALIGN
     y = torch.zeros(2, 1, 2, 128)
@@ -318,3 +323,20 @@ def test_descriptor_refuses_k_of_another_batch_or_head_size():
         _lib.make_desc(q, torch.zeros(2, 64, 128))
     d = _lib.make_desc(q, torch.zeros(2, 32, 2, 128))  # other length and head count: the ABI's business
     assert (d.batch, d.heads_q, d.heads_kv, d.seqlen_q, d.seqlen_k) == (2, 4, 2, 64, 32)
+
+
+def test_descriptor_output_strides_independent_of_q():
+    """q may be a strided view (a slice of a packed [B, S, 3, H, D] projection) while the outputs
+    are dense: q_stride comes from q, o_stride from o, kv_stride from k."""
+    import torch
+    B, S, H, D = 2, 64, 4, 128
+    packed = torch.zeros(B, S, 3, H, D)
+    q, k = packed[:, :, 0], packed[:, :, 1]
+    o = torch.zeros(B, S, H, D)
+    d = _lib.make_desc(q, k, o)
+    assert tuple(d.q_stride) == (S * 3 * H * D, 3 * H * D, D)
+    assert tuple(d.kv_stride) == (S * 3 * H * D, 3 * H * D, D)
+    assert tuple(d.o_stride) == (S * H * D, H * D, D)
+    assert tuple(_lib.make_desc(q, k).o_stride) == tuple(d.q_stride)  # no o: q's own strides
+    with pytest.raises(ValueError, match="shape"):
+        _lib.make_desc(q, k, torch.zeros(B, S + 1, H, D))

@@ -70,17 +70,17 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # the 1 GiB copy: the fetch counter reports half the bytes, the write counter all of them
     _counters_db(str(tmp_path / "cf" / "a_results.db"), [(1, "copy", "FETCH_SIZE", 524288.0), (2, "fill", "FETCH_SIZE", 8.0)])
     _counters_db(str(tmp_path / "cw" / "a_results.db"), [(1, "copy", "WRITE_SIZE", 1048576.0)])
-    out = str(tmp_path / "traffic.json")
-    bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"), out)
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    bench.traffic_summary("fwd", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"))
+    out = str(tmp_path / "fwd_kernel_d128_traffic.json")
     rec = json.load(open(out))
     assert rec["copy_calibration"]["fetch_scale"] == 2.0 and rec["copy_calibration"]["write_scale"] == 1.0
-    assert rec["fetch_size_kib_per_dispatch"] == [100.0, 300.0]
+    per = rec["per_kernel"]["fwd_kernel<128>"]
+    assert per["fetch_size_kib_per_dispatch"] == [100.0, 300.0]
     assert rec["hbm_fetch_bytes_per_launch"] == 200 * 1024 * 2
     assert rec["hbm_write_bytes_per_launch"] == 50 * 1024
     assert rec["hbm_bytes_per_launch"] == 200 * 1024 * 2 + 50 * 1024
     # the bench line reports the record only while the kernel source is the one it was taken on
-    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
-    os.replace(out, str(tmp_path / "fwd_kernel_d128_traffic.json"))
     wl = "llama2_7b_s32k_ring8"
     assert rec["workload"].split(" ")[0] == wl
     assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC, wl) == rec["hbm_bytes_per_launch"]
@@ -90,6 +90,40 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     json.dump(rec, open(str(tmp_path / "fwd_kernel_d128_traffic.json"), "w"))
     assert bench._traffic("fwd_kernel_d128", bench.FWD_SRC, wl) is None
     assert bench._traffic("no_such_kernel", bench.FWD_SRC, wl) is None
+
+
+def test_backward_traffic_is_summed_per_call(tmp_path, monkeypatch):
+    """Target bwd: one blockattn_bwd call launches a dK/dV and a dQ kernel (and delta on the first
+    call); bytes per call = all their bytes over the number of calls (dQ launches)."""
+    kv, dq, de = ("void ba::bwd_dkdv_kernel<128>(ba::BwdArgs)", "void ba::bwd_dq_kernel<128>(ba::BwdArgs)",
+                  "void ba::bwd_delta_kernel<128>(ba::BwdArgs, long)")
+    _counters_db(str(tmp_path / "f" / "a_results.db"),
+                 [(1, de, "FETCH_SIZE", 10.0), (2, kv, "FETCH_SIZE", 100.0), (3, dq, "FETCH_SIZE", 50.0),
+                  (4, kv, "FETCH_SIZE", 100.0), (5, dq, "FETCH_SIZE", 50.0),
+                  (6, "void ba::fwd_kernel<128>(ba::FwdArgs)", "FETCH_SIZE", 1e6)])
+    _counters_db(str(tmp_path / "w" / "a_results.db"),
+                 [(1, de, "WRITE_SIZE", 1.0), (2, kv, "WRITE_SIZE", 20.0), (3, dq, "WRITE_SIZE", 30.0),
+                  (4, kv, "WRITE_SIZE", 20.0), (5, dq, "WRITE_SIZE", 30.0)])
+    _counters_db(str(tmp_path / "cf" / "a_results.db"), [(1, "copy", "FETCH_SIZE", 1048576.0)])
+    _counters_db(str(tmp_path / "cw" / "a_results.db"), [(1, "copy", "WRITE_SIZE", 1048576.0)])
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    bench.traffic_summary("bwd", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"))
+    rec = json.load(open(str(tmp_path / "bwd_kernels_d128_traffic.json")))
+    assert rec["hbm_fetch_bytes_per_call"] == (10 + 200 + 100) * 1024 // 2
+    assert rec["hbm_write_bytes_per_call"] == (1 + 40 + 60) * 1024 // 2
+    assert rec["per_kernel"]["bwd_dkdv_kernel<128>"]["dispatches"] == 2
+    wl = "llama2_13b_s64k_ring8_train"
+    assert bench._traffic("bwd_kernels_d128", bench.BWD_SRC, wl, field="hbm_bytes_per_call") == rec["hbm_bytes_per_call"]
+
+
+def test_backward_algorithmic_bytes_small_case():
+    """bwd_algorithmic_bytes against a hand count: S=4, 2 chunks of 2, one head, D=8."""
+    from workloads.configs import Workload
+    w = Workload("t", 1, 1, 1, 4, 8, n_chunks=2, backward=True)
+    # chunk 0: 4 rows x (8*(2+2) + 8 + 8*8) = 4 * 104; K, V read and dK, dV written: 2 keys x 8 x 2 B x 4
+    # chunk 1: 2 rows x 104 + 2 x 8 x 2 x 4; once: delta 4 x (8*2*2 + 4), final dQ 4 x 8 x 2
+    want = (4 * 104 + 128 + 2 * 104 + 128 + 4 * 36 + 64) / 2
+    assert bench.bwd_algorithmic_bytes(w) == want
 
 
 def test_missing_profile_directory_is_reported(tmp_path):

@@ -111,22 +111,61 @@ def test_s2_backward(B, Hq, Hkv, shift_head0, D):
     _check_grads(f"s2 bwd B{B} Hq{Hq} Hkv{Hkv} D{D} shift_head0={shift_head0}", got, ref)
 
 
-def test_s2_backward_llama2_7b_s8k_heads_subset():
-    """S2 workload shape (S=8192, G=2048, 32 heads, heads 16-31 shifted) on 4 of its heads.
+def _oracle_s2_head_pairs(q, k, v, do, group, shift_head0, workers=8):
+    """The oracle's forward pair and gradients for every head of an S2 problem, computed on
+    pairs of heads (h, shift_head0 + h) so that each call holds one unshifted and one shifted
+    head (heads are independent in MHA); calls run on a thread pool (numpy releases the GIL in
+    its products and ufuncs), each with few BLAS threads."""
+    from concurrent.futures import ThreadPoolExecutor
 
-    Heads are independent in MHA, so heads {0, 15, 16, 31} (two unshifted, two
-    shifted) are a faithful subset; shift_head0 becomes 2 inside the subset.
-    """
+    from threadpoolctl import threadpool_limits
+    B, S, H, D = q.shape
+    assert 2 * shift_head0 == H
+    out = {}
+
+    def one(h):
+        idx = [h, shift_head0 + h]
+        sl = lambda a: np.ascontiguousarray(a[:, :, idx])
+        dq, dk, dv, o, lse = attention_backward(sl(q), sl(k), sl(v), sl(do), s2=S2Spec(group, 1, S),
+                                                row_block=1024)
+        return h, (dq, dk, dv, o, lse)
+    with threadpool_limits(limits=2):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            for h, r in ex.map(one, range(shift_head0)):
+                out[h] = r
+    return out
+
+
+def test_s2_llama2_7b_s8k_all_heads_forward_and_backward():
+    """S2 workload at its own shape (S=8192, G=2048, 32 heads, heads 16-31 rolled by 1024): the
+    forward O (fp32, max-abs) and LSE on every element of every head, the bf16 O as the RNE of the
+    fp32 one, and dQ, dK, dV on every head by relative L2, against the oracle's S2 mode."""
     w = get("s2attn_llama2_7b_s8k_g2048")
     q, k, v, do = make_inputs(w.batch, w.seqlen, w.heads_q, w.heads_kv, w.head_dim, seed=w.seed, with_dout=True)
-    heads = [0, 15, 16, 31]
-    sub = [t[:, :, heads].contiguous() for t in (q, k, v, do)]
-    qd, kd, vd, dod = _to_dev(*sub)
-    o, lse = ba.s2_forward(qd, kd, vd, w.s2_group, 2)
-    got = ba.s2_backward(qd, kd, vd, o, dod, lse, w.s2_group, 2)
+    qd, kd, vd, dod = _to_dev(q, k, v, do)
+    o32, lse = ba.s2_forward(qd, kd, vd, w.s2_group, w.s2_shift_head0, o_dtype=torch.float32)
+    o16, lse16 = ba.s2_forward(qd, kd, vd, w.s2_group, w.s2_shift_head0)
+    dq, dk, dv = ba.s2_backward(qd, kd, vd, o16, dod, lse16, w.s2_group, w.s2_shift_head0)
     torch.cuda.synchronize()
-    ref = attention_backward(*(f64(t) for t in sub), s2=S2Spec(w.s2_group, 2, w.seqlen))[:3]
-    _check_grads("s2 bwd S=8192 G=2048 heads {0,15,16,31}", got, ref)
+    assert torch.equal(lse, lse16)
+    assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16)), "bf16 O is not the RNE of the fp32 O"
+    log("S2 8192/2048 all heads: oracle (16 pairs of heads on a thread pool)")
+    qn, kn, vn, don = (t.float().numpy().astype(np.float64) for t in (q, k, v, do))
+    ref = _oracle_s2_head_pairs(qn, kn, vn, don, w.s2_group, w.s2_shift_head0)
+    o32n, lsen = f64(o32), f64(lse)
+    eo = el = eg = 0.0
+    for h, (rdq, rdk, rdv, ro, rl) in ref.items():
+        idx = [h, w.s2_shift_head0 + h]
+        eo = max(eo, float(np.abs(o32n[:, :, idx] - ro).max()))
+        el = max(el, float(np.abs(lsen[:, idx] - rl).max()))
+        for j, hh in enumerate(idx):
+            for g, r in ((dq, rdq), (dk, rdk), (dv, rdv)):
+                eg = max(eg, rel_l2(g[:, :, hh], r[:, :, j]))
+    e16 = float(np.abs(f64(o16) - np.concatenate(
+        [ref[h][3][:, :, :1] for h in range(16)] + [ref[h][3][:, :, 1:] for h in range(16)], axis=2)).max())
+    log(f"S2 8192/2048 all 32 heads: max|O-ref| {eo:.3e} (bf16 O {e16:.3e}), max|LSE-ref| {el:.3e}, "
+        f"worst per-head rel L2 of dQ/dK/dV {eg:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3 and eg <= TOL_GRAD
 
 
 def test_backward_full_size_one_head_and_sampled_rows():
@@ -282,3 +321,59 @@ def test_query_block_at_an_offset_forward_and_backward():
     assert eo <= 1e-2 and el <= 1e-3
     _check_grads("query block at an offset", (dq, dk, dv), (dq_r[:, a0:a1], dk_r, dv_r))
     assert not dk[:, 750:].float().abs().max().item() and not dv[:, 750:].float().abs().max().item()
+
+
+def test_ring_on_packed_qkv_views_with_dense_outputs():
+    """q, k, v are slices of one packed [B, S, 3, H, D] projection (strided views) while the ring
+    helpers' outputs are dense: q_stride, kv_stride and o_stride differ in the call.  Forward pair
+    and gradients against the oracle; dk, dv come back in k's (strided) layout."""
+    B, S, H, D, n = 2, 700, 4, 128, 3
+    q, k, v, do = make_inputs(B, S, H, H, D, seed=71, with_dout=True)
+    packed = torch.stack([q, k, v], dim=2).to(dev())
+    qv, kv, vv = packed[:, :, 0], packed[:, :, 1], packed[:, :, 2]
+    assert not qv.is_contiguous()
+    order = chunk_order(n, seed=5)
+    out, lse, o_acc = ba.ring_forward(qv, kv, vv, n, order)
+    assert o_acc.is_contiguous() and out.is_contiguous()
+    dq, dk, dv = ba.ring_backward(qv, kv, vv, out, do.to(dev()), lse, n, order)
+    torch.cuda.synchronize()
+    assert dk.stride() == kv.stride() and dq.is_contiguous()
+    from oracle import attention_forward
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    eo = float(np.abs(f64(o_acc) - o_ref).max())
+    el = float(np.abs(f64(lse) - l_ref).max())
+    log(f"packed views, dense outputs, ring n={n}: max|O-ref| {eo:.3e} max|LSE-ref| {el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do))[:3]
+    _check_grads("packed views, dense outputs, ring backward", (dq, dk, dv), ref)
+
+
+def test_dense_q_with_strided_outputs():
+    """The reverse: dense q, k, v with every query-shaped output a slice of a packed buffer."""
+    B, S, H, D = 1, 513, 2, 64
+    q, k, v, do = make_inputs(B, S, H, H, D, seed=72, with_dout=True)
+    qd, kd, vd = _to_dev(q, k, v)
+    f32 = torch.full((B, S, 2, H, D), float("nan"), device=dev())
+    b16 = torch.full((B, S, 4, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
+    o_acc, dq_acc = f32[:, :, 0], f32[:, :, 1]
+    out, dov, dq = b16[:, :, 0], b16[:, :, 1], b16[:, :, 2]
+    dov.copy_(do.to(dev()))
+    dq_acc.zero_()
+    lse = torch.empty(B, H, S, device=dev())
+    delta = torch.empty(B, H, S, device=dev())
+    dk = torch.empty_like(kd)
+    dv = torch.empty_like(vd)
+    ba.blockattn_fwd(qd, kd, vd, o_acc, lse, o_final=out)
+    ba.blockattn_bwd(qd, kd, vd, out, dov, lse, delta, dq_acc, dk, dv, dq_final=dq,
+                     flags=ba.BA_BWD_COMPUTE_DELTA | ba.BA_BWD_FINALIZE_DQ)
+    torch.cuda.synchronize()
+    from oracle import attention_forward
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    eo = float(np.abs(f64(o_acc) - o_ref).max())
+    el = float(np.abs(f64(lse) - l_ref).max())
+    log(f"dense q, strided outputs: max|O-ref| {eo:.3e} max|LSE-ref| {el:.3e}")
+    assert eo <= 1e-2 and el <= 1e-3
+    ref = attention_backward(f64(q), f64(k), f64(v), f64(do))[:3]
+    _check_grads("dense q, strided outputs", (dq, dk, dv), ref)
+    # the interleaved slices no call writes are untouched
+    assert torch.isnan(b16[:, :, 3]).all()
