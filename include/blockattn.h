@@ -61,7 +61,8 @@ typedef enum {
   BA_ERR_UNSUPPORTED = 5, /* head_dim not in {64, 128}, or an unknown dtype */
   BA_ERR_S2 = 6,          /* invalid S2 layout (see ba_s2_desc) */
   BA_ERR_MODE = 7,        /* unknown mode/flags, or ACCUMULATE with a non-fp32 o */
-  BA_ERR_LAUNCH = 8       /* the HIP runtime rejected a launch */
+  BA_ERR_LAUNCH = 8,      /* the HIP runtime rejected a launch */
+  BA_ERR_WORKSPACE = 9    /* blockattn_bwd_noalloc: the problem exceeds the static scratch buffer */
 } ba_status;
 
 typedef enum { BA_F32 = 0, BA_BF16 = 1 } ba_dtype;
@@ -158,6 +159,26 @@ int blockattn_bwd(const ba_desc* desc, const void* q, const void* k, const void*
                   const void* o, const void* dout, const float* lse, float* delta,
                   float* dq_acc, void* dk, void* dv, int32_t dkv_dtype, void* dq_final,
                   int32_t flags, hipStream_t stream);
+
+/* Allocation-free variant of blockattn_bwd, for callers that cannot allocate
+ * device memory or take workspace arguments (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments and results
+ * as blockattn_bwd without `delta`: the delta rows live in a static device
+ * buffer of the library (`scratch`, BLOCKATTN_NOALLOC_MAX_ROWS fp32 values =
+ * 32 MiB, one per GPU, held until the process ends) and are computed on EVERY
+ * call (BA_BWD_COMPUTE_DELTA is implied; FINALIZE_DQ is honoured), so each call
+ * stands alone and its outputs equal blockattn_bwd's bit for bit.  The buffer
+ * of the calling thread's current device (hipGetDevice) is used; every call on
+ * that GPU shares it, so calls that overlap on one GPU (other streams, other
+ * threads) race.  Calls no hipMalloc/hipFree.  Errors: those of blockattn_bwd,
+ * plus BA_ERR_WORKSPACE (checked before anything is enqueued) when
+ * batch * heads_q * seqlen_q exceeds BLOCKATTN_NOALLOC_MAX_ROWS or the buffer's
+ * device address cannot be obtained. */
+#define BLOCKATTN_NOALLOC_MAX_ROWS (1LL << 23)
+int blockattn_bwd_noalloc(const ba_desc* desc, const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse, float* dq_acc,
+                          void* dk, void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags,
+                          hipStream_t stream);
 
 /* S2-Attn forward over the whole sequence (one shot, no ring chunks):
  * o (dtype o_dtype) and lse are overwritten for every row, at original

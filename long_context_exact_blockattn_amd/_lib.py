@@ -20,6 +20,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "blockattn.h")
 BA_OK = 0
 BA_ERR_NULL, BA_ERR_SHAPE, BA_ERR_STRIDE, BA_ERR_ALIGN = 1, 2, 3, 4
 BA_ERR_UNSUPPORTED, BA_ERR_S2, BA_ERR_MODE, BA_ERR_LAUNCH = 5, 6, 7, 8
+BA_ERR_WORKSPACE = 9
+NOALLOC_MAX_ROWS = 1 << 23  # BLOCKATTN_NOALLOC_MAX_ROWS
 BA_F32, BA_BF16 = 0, 1
 BA_OVERWRITE, BA_ACCUMULATE = 0, 1
 BA_BWD_COMPUTE_DELTA, BA_BWD_FINALIZE_DQ = 1, 2
@@ -76,6 +78,8 @@ def load():
     lib.lse_merge.restype = ctypes.c_int
     lib.blockattn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
     lib.blockattn_bwd.restype = ctypes.c_int
+    lib.blockattn_bwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
+    lib.blockattn_bwd_noalloc.restype = ctypes.c_int
     lib.s2attn_fwd.argtypes = [D, S2, P, P, P, P, i32, P, P]
     lib.s2attn_fwd.restype = ctypes.c_int
     lib.s2attn_bwd.argtypes = [D, S2, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P]
@@ -281,6 +285,18 @@ def blockattn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, dq_final=None
                               _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk), _ptr(dv),
                               _dtype_code(dk, "dk"), _ptr(dq_final), int(flags), _stream(stream))
     _check(st, "blockattn_bwd")
+
+
+def blockattn_bwd_noalloc(q, k, v, o, dout, lse, dq_acc, dk, dv, *, dq_final=None, flags=0, q_pos0=0,
+                          k_pos0=0, causal=True, scale=None, stream=None):
+    """blockattn_bwd with its delta rows in the library's static device buffer (no workspace
+    argument, no allocation); delta is computed on every call.  See include/blockattn.h."""
+    _check_bwd(q, k, v, o, dout, lse, None, dq_acc, dk, dv, dq_final)
+    desc = make_desc(q, k, o, q_pos0=q_pos0, k_pos0=k_pos0, causal=causal, scale=scale)
+    st = load().blockattn_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                      _ptr(lse), _ptr(dq_acc), _ptr(dk), _ptr(dv), _dtype_code(dk, "dk"),
+                                      _ptr(dq_final), int(flags), _stream(stream))
+    _check(st, "blockattn_bwd_noalloc")
 
 
 def s2attn_bwd(q, k, v, o, dout, lse, delta, dq_acc, dk, dv, *, group, shift_head0, dq_final=None,

@@ -36,7 +36,7 @@ def build_example(verbose=False):
 def build_library(verbose=False):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, os.path.join(CSRC, "blockattn.hip"), "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, os.path.join(CSRC, "blockattn.hip"), os.path.join(CSRC, "noalloc.hip"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -260,6 +260,15 @@ int gemm_launch(int epi, const void* a, const void* b, const void* b3, void* c, 
 
 }  // namespace
 
+// Entry for the allocation-free variant (noalloc.hip), which brings its own delta buffer.
+__attribute__((visibility("hidden"))) int ba_bwd_impl(const ba_desc* d, const void* q, const void* k,
+                                                      const void* v, const void* o, const void* dout,
+                                                      const float* lse, float* delta, float* dq_acc, void* dk,
+                                                      void* dv, int32_t dkv_dtype, void* dq_final, int32_t flags,
+                                                      hipStream_t stream) {
+  return bwd_impl(d, nullptr, q, k, v, o, dout, lse, delta, dq_acc, dk, dv, dkv_dtype, dq_final, flags, stream);
+}
+
 extern "C" {
 
 int blockattn_fwd(const ba_desc* desc, const void* q, const void* k, const void* v, void* o,
@@ -358,6 +367,9 @@ const char* blockattn_status_string(int status) {
     case BA_ERR_S2: return "BA_ERR_S2: invalid S2 layout";
     case BA_ERR_MODE: return "BA_ERR_MODE: invalid mode/flags (ACCUMULATE needs an fp32 o)";
     case BA_ERR_LAUNCH: return "BA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case BA_ERR_WORKSPACE:
+      return "BA_ERR_WORKSPACE: the problem needs more than the library's static scratch buffer holds, "
+             "or its address could not be obtained";
     default: return "unknown blockattn status";
   }
 }

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = _lib.status_string(code)
         assert s.startswith("BA_"), s
     assert "unknown" in _lib.status_string(99)
@@ -340,3 +340,17 @@ def test_descriptor_output_strides_independent_of_q():
     assert tuple(_lib.make_desc(q, k).o_stride) == tuple(d.q_stride)  # no o: q's own strides
     with pytest.raises(ValueError, match="shape"):
         _lib.make_desc(q, k, torch.zeros(B, S + 1, H, D))
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch_buffer(lib):
+    """blockattn_bwd_noalloc checks the problem against its static buffer before anything else
+    touches the GPU (so this runs without one)."""
+    P = ctypes.c_void_p
+    d = _desc(B=1, Hq=64, Hkv=8, Sq=(1 << 17) + 1, Sk=256)
+    st = lib.blockattn_bwd_noalloc(ctypes.byref(d), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                   P(FAKE), P(FAKE), P(FAKE), _lib.BA_BF16, None, 0, None)
+    assert st == _lib.BA_ERR_WORKSPACE
+    assert "scratch" in _lib.status_string(st)
+    assert lib.blockattn_bwd_noalloc(None, *([P(FAKE)] * 9), _lib.BA_BF16, None, 0, None) == _lib.BA_ERR_NULL
+    d = _desc(Sq=-1)
+    assert lib.blockattn_bwd_noalloc(ctypes.byref(d), *([P(FAKE)] * 9), _lib.BA_BF16, None, 0, None) == _lib.BA_ERR_SHAPE
