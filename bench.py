@@ -219,7 +219,7 @@ def side_measurements(w, tensors, reps=5):
     return res
 
 
-def run_training(w, steps, warmup, tensors=None):
+def run_training(w, steps, warmup, tensors=None, one_shot=True):
     """Ring forward + ring backward (training step of attention), or S2 forward + backward.
 
     Every library call is bracketed by HIP events on the working stream, so the per-call (per
@@ -312,7 +312,7 @@ def run_training(w, steps, warmup, tensors=None):
     assert not torch.isnan(dq).any() and not torch.isnan(dk).any(), "NaN in gradients"
     res = {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "order": order, "calls_per_phase": n,
            "fwd_call_ms": fwd_call_ms, "bwd_call_ms": bwd_call_ms}
-    if w.s2_group is None and n > 1:
+    if one_shot and w.s2_group is None and n > 1:
         def bwd_one_shot():
             dq_acc.zero_()
             _lib.blockattn_bwd(q, k, v, o, do, lse, delta, dq_acc, dk, dv, dq_final=dq,
@@ -407,7 +407,7 @@ def cpu_baseline(w, budget_flop=1.2e12, rows_budget_flop=1.5e11):
             **_cpu_info()}
 
 
-def cpu_baseline_backward(w, prefix=12288):
+def cpu_baseline_backward(w, prefix=20480):
     """The oracle's backward as it stands, on a bounded sample of a causal training workload: the
     first `prefix` positions of query heads 0..n-1 (one head per pool thread).  A causal prefix is
     a complete attention problem of its own (its rows see only its keys), so this is the same
@@ -566,7 +566,7 @@ TRAFFIC_TARGETS = {
             "fwd_kernel_d128_traffic.json", "hbm_bytes_per_launch"),
     "bwd": (("bwd_dkdv_kernel<128>", "bwd_dq_kernel<128>", "bwd_delta_kernel<128>"), "bwd_dq_kernel<128>",
             "llama2_13b_s64k_ring8_train", BWD_SRC,
-            "--workload llama2_13b_s64k_ring8_train --steps 1 --warmup 0 --no-cpu-baseline",
+            "--workload llama2_13b_s64k_ring8_train --steps 1 --warmup 0 --no-cpu-baseline --no-side-measurements",
             "bwd_kernels_d128_traffic.json", "hbm_bytes_per_call"),
 }
 
@@ -712,13 +712,13 @@ def bwd_algorithmic_bytes(w):
     return tot / n
 
 
-def training_record(w, steps, warmup, cpu=True, tensors=None):
+def training_record(w, steps, warmup, cpu=True, tensors=None, side=True):
     """Forward + backward of a training workload: phase times and rates, the backward's roofline
     per blockattn_bwd call (one ring step: its dK/dV and dQ launches, plus the delta launch on the
     first step), the backward as one call against the ring, and the oracle's backward on a bounded
     sample as the CPU baseline."""
     import statistics
-    r = run_training(w, steps, warmup, tensors=tensors)
+    r = run_training(w, steps, warmup, tensors=tensors, one_shot=side)
     ms = r["wall_s"] * 1e3 / steps
     fwd_med, bwd_med = statistics.median(r["fwd_ms"]), statistics.median(r["bwd_ms"])
     n = r["calls_per_phase"]
@@ -755,7 +755,8 @@ def training_record(w, steps, warmup, cpu=True, tensors=None):
 
 def training_line(w, args):
     """One JSON line for a forward+backward workload (attention training step)."""
-    rec = training_record(w, args.steps, args.warmup, cpu=not args.no_cpu_baseline)
+    rec = training_record(w, args.steps, args.warmup, cpu=not args.no_cpu_baseline,
+                          side=not args.no_side_measurements)
     tflops = rec["step_tflops"]
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
@@ -788,7 +789,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters)")
     ap.add_argument("--no-side-measurements", action="store_true",
-                    help="skip the one-chunk forward and the HBM-bound kernel timings (for profiled runs)")
+                    help="skip the one-chunk forward / backward and the HBM-bound kernel timings (for "
+                         "profiled runs)")
     ap.add_argument("--counter-summary", metavar="DIR",
                     help="print MFMA-busy and VALU-busy of the forward kernel from a rocprofv3 --pmc run "
                          "with the counters in bench.COUNTERS")
