@@ -46,6 +46,8 @@ struct BwdArgs {
   int32_t dkv_f32, finalize;
   float scale, scale_log2;
   int64_t n_tiles;  // query tiles (dq_kernel) or key tiles (dkdv_kernel) per head
+  int64_t n_ranks;  // dq_kernel: of the query tiles, the n_ranks longest are launched (the rest
+                    // have no allowed key and, unless finalizing, nothing to do)
   int64_t n_items;
 };
 
@@ -152,8 +154,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
-  const int64_t bh = pid / a.n_tiles;
-  const int64_t w = pid % a.n_tiles;
+  const int64_t bh = pid / a.n_ranks;
+  const int64_t w = pid % a.n_ranks;
   const int b = (int)(bh / a.Hq);
   const int h = (int)(bh % a.Hq);
   const int kvh = h / a.grp;

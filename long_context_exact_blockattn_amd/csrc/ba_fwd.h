@@ -181,14 +181,32 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
       if (a.causal && t.cpos0 > wave_cmax) return;  // every key after every row of this wave
       // ---- S^T = K Q^T  (two 32-key blocks; each K fragment feeds QB MFMAs)
       f32x16 s[QB][2];
+      {
+        // the two 32-key blocks' fragments of k-step kk + 2 are read while the MFMAs of
+        // k-step kk run (three fragment sets live)
+        bf16x8 kf[3][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int j = 0; j < 2; ++j) {
+          kf[j][0] = *(const bf16x8*)(Ks + k_off[j]);
+          kf[j][1] = *(const bf16x8*)(Ks + 32 * D + k_off[j]);
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf = *(const bf16x8*)(Ks + kb * 32 * D + k_off[kk]);
+          if (kk + 2 < KK) {
+            kf[(kk + 2) % 3][0] = *(const bf16x8*)(Ks + k_off[kk + 2]);
+            kf[(kk + 2) % 3][1] = *(const bf16x8*)(Ks + 32 * D + k_off[kk + 2]);
+          }
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = mfma32(kf, qf[qb][kk], kk == 0 ? f32x16{} : s[qb][kb]);
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              s[qb][kb] = mfma32(kf[kk % 3][kb], qf[qb][kk], kk == 0 ? f32x16{} : s[qb][kb]);
+        }
+        // keep that order: 4 reads, then per k-step 2 reads (k-step + 2) before 2 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 2 < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
       // ---- mask: keys past the chunk's end or (causal) after this lane's row

@@ -174,6 +174,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.finalize = finalize;
   a.scale = scale_of(d);
   a.scale_log2 = a.scale * kLog2e;
+  a.n_tiles = a.n_ranks = a.n_items = 0;
   const bool d128 = d->head_dim == 128;
 
   if ((flags & BA_BWD_COMPUTE_DELTA) && d->seqlen_q > 0) {
@@ -200,8 +201,32 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   if (d->seqlen_q > 0) {
     BwdArgs b = a;
     b.n_tiles = ceil_div(d->seqlen_q, kDqBM);
-    b.n_items = (int64_t)d->batch * d->heads_q * b.n_tiles;
+    // causal query tiles wholly before the chunk have no allowed key (they are the last
+    // ranks of the longest-first order) and are not launched; when finalizing, their bf16 dQ
+    // is a plain conversion of the accumulator
+    int64_t skip_qt = 0;
+    if (!s2 && d->causal) {
+      int64_t first_row = d->seqlen_k > 0 ? d->k_pos0 - d->q_pos0 : d->seqlen_q;
+      first_row = first_row < 0 ? 0 : (first_row > d->seqlen_q ? d->seqlen_q : first_row);
+      skip_qt = first_row / kDqBM;
+    }
+    b.n_ranks = b.n_tiles - skip_qt;
+    b.n_items = (int64_t)d->batch * d->heads_q * b.n_ranks;
     if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
+    if (finalize && skip_qt > 0) {
+      StoreArgs st;
+      st.o_acc = dq_acc;
+      st.o_final = (bf16*)dq_final;
+      st.s_b = d->o_stride[0]; st.s_s = d->o_stride[1]; st.s_h = d->o_stride[2];
+      st.rows = skip_qt * kDqBM;
+      st.Hq = d->heads_q; st.D = d->head_dim;
+      st.n_threads = (int64_t)d->batch * st.rows * d->heads_q * (d->head_dim / 8);
+      const int64_t blocks = ceil_div(st.n_threads, 256);
+      if (blocks > 0x7fffffffLL) return BA_ERR_SHAPE;
+      hipLaunchKernelGGL(store_final_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, st);
+      if ((r = launched())) return r;
+    }
+    if (b.n_items == 0) return BA_OK;
     if (d128)
       hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)b.n_items), dim3(kBwdThreads), 0, stream, b);
     else
