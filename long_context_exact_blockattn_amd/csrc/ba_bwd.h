@@ -85,16 +85,15 @@ struct TileLoader {
     row0 = ci / CPR;
     col = 8 * ((ci % CPR) ^ swz<D>(row0));
   }
-  // src points at row 0 of the tile; rows are `stride` elements apart
+  // src points at row 0 of the tile; rows are `stride` elements apart.  Buffer loads over a
+  // resource spanning exactly the tile's valid rows: lanes of a ragged tile's missing rows
+  // read past its end and get zeros (masked by the caller).
   __device__ __forceinline__ void issue(const bf16* src, int stride, int rows, bf16* dst, int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int last = rows - 1;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, 2u * (unsigned)((rows - 1) * stride + D));
 #pragma unroll
-    for (int p = 0; p < NPI; ++p) {
-      int r = row0 + p * STEP;
-      r = r < last ? r : last;
-      g2lds16(src + (unsigned)(r * stride + col), dst + (p * NW + wave) * 512);
-    }
+    for (int p = 0; p < NPI; ++p)
+      buf2lds16(rs, 2u * (unsigned)((row0 + p * STEP) * stride + col), 0u, dst + (p * NW + wave) * 512);
 #endif
   }
 };

@@ -153,25 +153,15 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
       const KTile t = make_ktile(sc, kt);
       const bf16* kt_base = kbase + t.row0 * a.ks_s;
       const bf16* vt_base = vbase + t.row0 * a.ks_s;
-      const int last = (int)t.rows - 1;
-      if (last == BN - 1) {  // full tile: scalar base + the fixed per-lane offsets
-        // the resource spans exactly the tile's rows: (BN - 1) strides plus one row
-        const unsigned bytes = 2u * (unsigned)((BN - 1) * ks_s + D);
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kt_base, bytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt_base, bytes);
-#pragma unroll
-        for (int p = 0; p < NPI; ++p) {
-          buf2lds16(krs, g_off[p], 0u, kdst + (p * NW + wave) * 512);
-          buf2lds16(vrs, g_off[p], 0u, vdst + (p * NW + wave) * 512);
-        }
-        return;
-      }
+      // the resource spans exactly the tile's valid rows ((rows - 1) strides plus one row):
+      // lanes of a ragged tile's missing rows read past its end and get zeros (masked later)
+      const unsigned bytes = 2u * (unsigned)(((int)t.rows - 1) * ks_s + D);
+      const __amdgpu_buffer_rsrc_t krs = make_rsrc(kt_base, bytes);
+      const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt_base, bytes);
 #pragma unroll
       for (int p = 0; p < NPI; ++p) {
-        const int r = g_row[p] < last ? g_row[p] : last;  // ragged tail re-reads the last row
-        const unsigned off = (unsigned)(r * ks_s + g_col[p]);
-        g2lds16(kt_base + off, kdst + (p * NW + wave) * 512);
-        g2lds16(vt_base + off, vdst + (p * NW + wave) * 512);
+        buf2lds16(krs, g_off[p], 0u, kdst + (p * NW + wave) * 512);
+        buf2lds16(vrs, g_off[p], 0u, vdst + (p * NW + wave) * 512);
       }
     };
 
