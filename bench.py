@@ -558,6 +558,41 @@ def counter_summary(d, out=None, kernel=None):
             json.dump(rec, f, indent=1)
 
 
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_DATA_FIFO_FULL SQ_WAIT_INST_LDS "
+                "SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_VALU_MFMA_COEXEC_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS "
+                "GRBM_GUI_ACTIVE")
+
+
+def counter_table(d, kernel):
+    """Every counter of one rocprofv3 --pmc run for one kernel, summed over its dispatches, as a total
+    and per CU-cycle (cycles = GRBM_GUI_ACTIVE / 8, 256 CUs).  With LDS_COUNTERS this gives the LDS
+    utilisation (SQ_LDS_IDX_ACTIVE per CU-cycle), the LDS load bandwidth (SQ_INSTS_LDS_LOAD_BANDWIDTH
+    counts 64-byte units), the matrix cores' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES per CU-cycle / 4
+    SIMDs) and how often a vector instruction issues while the matrix core is busy
+    (SQ_VALU_MFMA_COEXEC_CYCLES, per SIMD)."""
+    import sqlite3
+    tot, disp = {}, set()
+    for db in _result_dbs(d):
+        con = sqlite3.connect(db)
+        for did, name, cname, val in con.execute(
+                "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if kernel in name:
+                disp.add((db, did))
+                tot[cname] = tot.get(cname, 0.0) + val
+    cu_cycles = tot["GRBM_GUI_ACTIVE"] / 8.0 * 256
+    print(f"{len(disp)} dispatches of {kernel}; per CU-cycle = total / (GRBM_GUI_ACTIVE / 8 x 256 CUs)")
+    for n in sorted(tot):
+        if n != "GRBM_GUI_ACTIVE":
+            print(f"  {n:30s} total {tot[n]:12.4g}  per CU-cycle {tot[n] / cu_cycles:8.4f}")
+    if "SQ_LDS_IDX_ACTIVE" in tot:
+        print(f"  LDS busy {tot['SQ_LDS_IDX_ACTIVE'] / cu_cycles:.3f} of cycles; LDS loads "
+              f"{64 * tot.get('SQ_INSTS_LDS_LOAD_BANDWIDTH', 0) / cu_cycles:.1f} B per CU-cycle")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in tot:
+        print(f"  MFMA busy {tot['SQ_VALU_MFMA_BUSY_CYCLES'] / cu_cycles / 4:.3f} of SIMD-cycles; vector "
+              f"instructions co-issued with a busy matrix core in "
+              f"{tot.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0) / cu_cycles / 4:.3f} of SIMD-cycles")
+
+
 TRAFFIC_TARGETS = {
     # key: (kernels summed per launch / call, the launch kernel counted once per call, workload,
     #       source file, bench arguments of the profiled run, summary file field)
@@ -796,6 +831,9 @@ def main():
                          "with the counters in bench.COUNTERS")
     ap.add_argument("--counter-kernel", metavar="NAME",
                     help="with --counter-summary: summarise this kernel instead of the forward (printed only)")
+    ap.add_argument("--counter-table", nargs=2, metavar=("DIR", "KERNEL"),
+                    help="print every counter of a rocprofv3 --pmc run (e.g. bench.LDS_COUNTERS) for one kernel, "
+                         "total and per CU-cycle")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel statistics of a rocprofv3 --kernel-trace output directory")
     ap.add_argument("--traffic-summary", nargs=5, metavar=("TARGET", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -812,6 +850,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_table:
+        counter_table(*args.counter_table)
         return
     if args.traffic_summary:
         if args.traffic_summary[0] not in TRAFFIC_TARGETS:

@@ -69,16 +69,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 // Direct buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
 // the address is the resource base (scalar registers) plus a per-lane byte
 // offset (plus a scalar offset), so a tile's loads need no per-lane address
-// arithmetic.  As for g2lds16, lane L writes lds_base + 16*L.
+// arithmetic; lane L of the wave writes lds_base + 16*L (lds_base the same for
+// every lane), and a lane whose offset lies past the resource's size reads
+// zeros.  Every tile load uses this form: with the FLAT form
+// (global_load_lds) in flight the compiler can no longer count the wave's
+// outstanding LDS reads and waits for all of them before each use.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff, 0, 0);
-}
-
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane L of the wave writes lds_base + 16*L, whatever global address it reads.
-// lds_base must be the same for every lane of the wave.
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(0): this wave's outstanding vector-memory loads (including

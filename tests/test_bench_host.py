@@ -166,3 +166,17 @@ def test_step_counts_are_checked():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "--steps" in r.stderr and r.stdout == ""
+
+
+def test_counter_table_normalises_per_cu_cycle(tmp_path, capsys):
+    k = "void ba::fwd_kernel<128>(ba::FwdArgs)"
+    # one dispatch of 1000 cycles on each of the 8 XCDs: 256 CUs x 1000 CU-cycles
+    rows = [(1, k, "GRBM_GUI_ACTIVE", 8000.0), (1, k, "SQ_LDS_IDX_ACTIVE", 64000.0),
+            (1, k, "SQ_INSTS_LDS_LOAD_BANDWIDTH", 256000.0), (1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0),
+            (1, k, "SQ_VALU_MFMA_COEXEC_CYCLES", 102400.0), (2, "other", "SQ_LDS_IDX_ACTIVE", 1e9)]
+    _counters_db(str(tmp_path / "p" / "a_results.db"), rows)
+    bench.counter_table(str(tmp_path / "p"), "fwd_kernel<128>")
+    out = capsys.readouterr().out
+    assert "1 dispatches of fwd_kernel<128>" in out
+    assert "LDS busy 0.250 of cycles; LDS loads 64.0 B per CU-cycle" in out
+    assert "MFMA busy 0.500 of SIMD-cycles" in out and "in 0.100 of SIMD-cycles" in out
