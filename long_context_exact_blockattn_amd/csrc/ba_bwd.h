@@ -303,12 +303,19 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
   if (!row_ok) return;
   const int64_t obase = ooff + 4 * hl;
+  // the lane's dq_acc row is read whole before any store: one memory round trip
+  // for the wave instead of one per 16-byte piece
+  f32x4 prev[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) prev[db][g] = *(const f32x4*)(a.dq_acc + obase + 32 * db + 8 * g);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t off = obase + 32 * db + 8 * g;
-      f32x4 val = *(const f32x4*)(a.dq_acc + off);
+      f32x4 val = prev[db][g];
       if (!empty) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(a.scale, dqacc[db][4 * g + e], val[e]);

@@ -295,66 +295,105 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
     }
   }
 
-  // ---- epilogue, per query block: partial pair of this chunk, optional merge
+  // ---- epilogue: the chunk's partial pair (acc / l, m + log2 l), merged in ACCUMULATE
+  // mode into the running pair.  Rows pass through LDS so that global memory is read and
+  // written in whole lines (in the MFMA layout one 16-byte access per lane touches 32
+  // rows): after the loop's last barrier the four tile buffers are free, and wave w
+  // stages its 32 rows x D fp32 in buffer w (32*4D bytes = one tile of BN x D bf16).  In
+  // the stage, row r's 16-byte piece c sits at slot c ^ (r mod D/4) of the row, so the
+  // MFMA-layout accesses (32 rows, one piece each) spread over the banks; the direct loads
+  // and the copy-out walk the stage linearly, 1 KB (whole rows) per instruction.
+  static_assert(QB == 1, "the epilogue is written for one 32-row block per wave");
+  constexpr int SPR = D / 4;               // 16-byte pieces per staged row
+  constexpr int NIO = 32 * SPR / 64;       // linear 1 KB steps per wave
+  const float l_tot = halves_sum(l_run[0]);
+  const bool has = l_tot > 0.f;
+  const float lse2_c = has ? m_run[0] + log2_hw(l_tot) : -INFINITY;
+  const float inv_l = has ? 1.f / l_tot : 0.f;
+  const int64_t wrows = qt.rows - (int64_t)wave * 32;
+  if (wrows <= 0) return;
+  const int vr = wrows < 32 ? (int)wrows : 32;  // rows of this wave inside the tile
+  float* const stage = (float*)(wave == 0 ? sK0 : wave == 1 ? sV0 : wave == 2 ? sK1 : sV1);
+  const int64_t gbase = (int64_t)b * a.os_b + (qt.row0 + (int64_t)wave * 32) * a.os_s + (int64_t)h * a.os_h;
+  const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + qt.row0 + rloc[0];
+  const bool write_state = !(a.accumulate && empty);
+  float ca = 0.f, cc = inv_l, L2 = lse2_c;
+  if (a.accumulate) {
+    // the running output's rows, straight into the stage (rows past the tile read zeros)
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc((const float*)a.o + gbase, 4u * (unsigned)((vr - 1) * (int)a.os_s + D));
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = halves_sum(l_run[qb]);
-    const bool has = l_tot > 0.f;
-    const float lse2_c = has ? m_run[qb] + log2_hw(l_tot) : -INFINITY;
-    const float inv_l = has ? 1.f / l_tot : 0.f;
-    if (!row_ok[qb]) continue;
-    const int64_t row = qt.row0 + rloc[qb];
-    const int64_t lse_idx = ((int64_t)b * a.Hq + h) * a.Sq + row;
-    const int64_t obase = (int64_t)b * a.os_b + row * a.os_s + (int64_t)h * a.os_h + 4 * hl;
-    float ca = 0.f, cc = inv_l, L2 = lse2_c;
-    if (a.accumulate) {
-      const float la2 = a.lse[lse_idx] * kLog2e;
-      const float M = fmaxf(la2, lse2_c);
-      if (M == -INFINITY) {
-        ca = 0.f; cc = 0.f; L2 = -INFINITY;
-      } else {
-        const float wa = exp2_hw(la2 - M);
-        const float wc = exp2_hw(lse2_c - M);
-        const float tot = wa + wc;
-        L2 = M + log2_hw(tot);
-        ca = wa / tot;
-        cc = wc / tot * inv_l;
-      }
+    for (int i = 0; i < NIO; ++i) {
+      const int u = i * 64 + lane, r = u / SPR, c = (u % SPR) ^ (r & (SPR - 1));
+      buf2lds16(rs, 4u * (unsigned)(r * (int)a.os_s + 4 * c), 0u, stage + 256 * i);
     }
-    const bool write_state = !(a.accumulate && empty);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t off = obase + 32 * db + 8 * g;
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = cc * oacc[qb][db][4 * g + e];
-        if (a.accumulate && ca > 0.f) {
-          const f32x4 prev = *(const f32x4*)((const float*)a.o + off);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = __builtin_fmaf(ca, prev[e], val[e]);
-        }
-        if (write_state) {
-          if (a.o_f32) {
-            *(f32x4*)((float*)a.o + off) = val;
-          } else {
-            bf16x4 bv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
-            *(bf16x4*)((bf16*)a.o + off) = bv;
-          }
-        }
-        if (a.o_final) {
-          bf16x4 bv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bv[e] = (bf16)val[e];
-          *(bf16x4*)(a.o_final + off) = bv;
-        }
-      }
+    const float la = row_ok[0] ? a.lse[lse_idx] : -INFINITY;
+    wait_vmem();
+    // a row whose running LSE is -inf gets weight 0 and its stale values are not used
+    const float la2 = la * kLog2e;
+    const float M = fmaxf(la2, lse2_c);
+    if (M == -INFINITY) {
+      ca = 0.f; cc = 0.f; L2 = -INFINITY;
+    } else {
+      const float wa = exp2_hw(la2 - M);
+      const float wc = exp2_hw(lse2_c - M);
+      const float tot = wa + wc;
+      L2 = M + log2_hw(tot);
+      ca = wa / tot;
+      cc = wc / tot * inv_l;
     }
-    if (write_state && hl == 0) a.lse[lse_idx] = L2 * kLn2;
   }
+  // merge in the MFMA layout: lane (row l32, half hl) holds pieces 8db + 2g + hl
+  auto stage_at = [&](int db, int g) __attribute__((always_inline)) {
+    const int c = 8 * db + 2 * g + hl;
+    return stage + 4 * (l32 * SPR + (c ^ (l32 & (SPR - 1))));
+  };
+  f32x4 prev[DB][4];
+  if (a.accumulate) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) prev[db][g] = *(const f32x4*)stage_at(db, g);
+  }
+  const bool use_prev = a.accumulate && ca > 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        val[e] = cc * oacc[0][db][4 * g + e];
+        val[e] = use_prev ? __builtin_fmaf(ca, prev[db][g][e], val[e]) : val[e];
+      }
+      *(f32x4*)stage_at(db, g) = val;
+    }
+  }
+  // the copy-out reads pieces other lanes of the wave wrote
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  f32x4 outv[NIO];
+#pragma unroll
+  for (int i = 0; i < NIO; ++i) outv[i] = *(const f32x4*)(stage + 4 * (i * 64 + lane));
+#pragma unroll
+  for (int i = 0; i < NIO; ++i) {
+    const int u = i * 64 + lane, r = u / SPR, c = (u % SPR) ^ (r & (SPR - 1));
+    const f32x4 v = outv[i];
+    if (r < vr) {
+      const int64_t go = gbase + (int64_t)r * a.os_s + 4 * c;
+      bf16x4 bv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = (bf16)v[e];
+      if (write_state) {
+        if (a.o_f32)
+          *(f32x4*)((float*)a.o + go) = v;
+        else
+          *(bf16x4*)((bf16*)a.o + go) = bv;
+      }
+      if (a.o_final) *(bf16x4*)(a.o_final + go) = bv;
+    }
+  }
+  if (write_state && hl == 0 && row_ok[0]) a.lse[lse_idx] = L2 * kLn2;
 #endif
 }
 
