@@ -49,6 +49,7 @@ struct BwdArgs {
   int64_t n_ranks;  // dq_kernel: of the query tiles, the n_ranks longest are launched (the rest
                     // have no allowed key and, unless finalizing, nothing to do)
   int64_t n_items;
+  int64_t hx;       // dq_kernel: heads interleaved per XCD (qitem_of_pid), 0 for head-major
 };
 
 constexpr int kDqBM = 128;   // query rows per dq item (4 waves x 32)
@@ -152,9 +153,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
 
-  const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
-  const int64_t bh = pid / a.n_ranks;
-  const int64_t w = pid % a.n_ranks;
+  int64_t bh, w;
+  qitem_of_pid(xcd_remap(blockIdx.x, a.n_items), a.n_ranks, a.hx, bh, w);
   const int b = (int)(bh / a.Hq);
   const int h = (int)(bh % a.Hq);
   const int kvh = h / a.grp;

@@ -42,6 +42,7 @@ struct FwdArgs {
   int64_t n_qtiles;  // query tiles per (batch, head)
   int64_t n_ranks;   // of which launched: the n_ranks longest (the rest have no allowed key)
   int64_t n_items;
+  int64_t hx;        // heads interleaved per XCD (qitem_of_pid), 0 for head-major order
 };
 
 // One 32-row query block per wave, two waves per SIMD.  The loops below are
@@ -76,9 +77,8 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
   const int l32 = lane & 31;
 
   // ---- work item
-  const int64_t pid = xcd_remap(blockIdx.x, a.n_items);
-  const int64_t bh = pid / a.n_ranks;
-  const int64_t w = pid % a.n_ranks;
+  int64_t bh, w;
+  qitem_of_pid(xcd_remap(blockIdx.x, a.n_items), a.n_ranks, a.hx, bh, w);
   const int b = (int)(bh / a.Hq);
   const int h = (int)(bh % a.Hq);
   const int kvh = h / a.grp;

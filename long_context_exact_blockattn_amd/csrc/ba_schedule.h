@@ -161,4 +161,37 @@ BA_HD int64_t xcd_remap(int64_t pid, int64_t n) {
   return pid < full ? (pid % 8) * per + pid / 8 : pid;
 }
 
+// (batch*head, rank) of logical item pid of a query-stationary launch with
+// n_ranks tiles per (batch, head).  Head-major by default: an XCD's slots work
+// through one head's tiles (longest first) before the next head's, so the
+// key/value rows they share stay in its L2.  When a launch has few ranks per
+// head (an XCD's 64 slots would see only a round or two of one head's tiles)
+// and its heads split evenly over the XCDs, the XCD's heads are taken in groups
+// of hx, each group rank-major: every head of the group starts its longest tile
+// first, so the launch is not left waiting on a late head's longest tile, while
+// only hx heads' keys and values are live in the XCD at a time.
+BA_HD void qitem_of_pid(int64_t pid, int64_t n_ranks, int64_t hx, int64_t& bh, int64_t& w) {
+  if (hx > 1) {
+    const int64_t per = hx * n_ranks;  // items of one group
+    const int64_t j = pid % per;
+    bh = (pid / per) * hx + j % hx;
+    w = j / hx;
+  } else {
+    bh = pid / n_ranks;
+    w = pid % n_ranks;
+  }
+}
+
+// Group size hx for qitem_of_pid, or 0 for head-major order: enough heads for two
+// rounds of an XCD's 64 workgroup slots (256 CUs in 8 XCDs, two workgroups each),
+// a divisor of the heads each XCD takes.
+inline int64_t interleave_heads(int64_t n_bh, int64_t n_ranks) {
+  if (n_ranks <= 0 || n_ranks >= 128 || n_bh % 8 != 0) return 0;
+  const int64_t per_xcd = n_bh / 8;
+  int64_t g = (128 + n_ranks - 1) / n_ranks;
+  if (g > per_xcd) g = per_xcd;
+  while (per_xcd % g != 0) --g;
+  return g;
+}
+
 }  // namespace ba

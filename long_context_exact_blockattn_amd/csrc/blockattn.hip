@@ -115,6 +115,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   }
   a.n_ranks = a.n_qtiles - skip_qt;
   a.n_items = (int64_t)d->batch * d->heads_q * a.n_ranks;
+  a.hx = interleave_heads((int64_t)d->batch * d->heads_q, a.n_ranks);
   if (a.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
   if (o_final && skip_qt > 0) {
     StoreArgs st;
@@ -174,7 +175,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.finalize = finalize;
   a.scale = scale_of(d);
   a.scale_log2 = a.scale * kLog2e;
-  a.n_tiles = a.n_ranks = a.n_items = 0;
+  a.n_tiles = a.n_ranks = a.n_items = a.hx = 0;
   const bool d128 = d->head_dim == 128;
 
   if ((flags & BA_BWD_COMPUTE_DELTA) && d->seqlen_q > 0) {
@@ -212,6 +213,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
     }
     b.n_ranks = b.n_tiles - skip_qt;
     b.n_items = (int64_t)d->batch * d->heads_q * b.n_ranks;
+    b.hx = interleave_heads((int64_t)d->batch * d->heads_q, b.n_ranks);
     if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
     if (finalize && skip_qt > 0) {
       StoreArgs st;

@@ -40,7 +40,7 @@ def _check_grads(tag, got, ref):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S,Hq,Hkv,causal", [(1000, 2, 2, True), (333, 8, 2, True), (300, 2, 2, False),
-                                             (64, 4, 1, True), (300, 1, 1, True)])
+                                             (64, 4, 1, True), (300, 1, 1, True), (1000, 16, 4, True)])
 def test_backward_one_shot(D, S, Hq, Hkv, causal):
     q, k, v, do = make_inputs(1, S, Hq, Hkv, D, seed=S + 7 * D, with_dout=True)
     got = _gpu_forward_backward(q, k, v, do, causal=causal)

@@ -47,8 +47,10 @@ def test_ring_small_d64_seeded_order():
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S,Hq,Hkv,causal", [(1000, 2, 2, True), (333, 8, 2, True), (777, 4, 4, False),
-                                             (128, 2, 1, True), (1, 2, 2, True), (300, 1, 1, True)])
+                                             (128, 2, 1, True), (1, 2, 2, True), (300, 1, 1, True),
+                                             (1000, 16, 4, True), (700, 24, 8, False)])
 def test_one_shot(D, S, Hq, Hkv, causal):
+    # 16 and 24 heads with few query tiles: the launch interleaves 2 and 3 heads per XCD
     q, k, v = make_inputs(1, S, Hq, Hkv, D, seed=S + D)
     qd, kd, vd = _to_dev(q, k, v)
     o = torch.full((1, S, Hq, D), float("nan"), device=dev())
@@ -84,6 +86,7 @@ def test_ring_orders_match_one_shot(n_chunks, S):
         order = chunk_order(n_chunks, seed=seed)
         out, lse, o_acc = ba.ring_forward(qd, kd, vd, n_chunks, order)
         torch.cuda.synchronize()
+        assert torch.equal(out, o_acc.to(torch.bfloat16))
         _check_pair(f"ring n={n_chunks} S={S} order={order}", o_acc, lse, o_ref, l_ref, out)
 
 
@@ -267,6 +270,28 @@ def test_full_size_ring_sampled(name):
     log(f"{name} order={order} heads={heads} rows={len(rows)}: O {worst_o:.3e} LSE {worst_l:.3e}")
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
     assert not torch.isnan(o_acc).any()
+
+
+def test_one_shot_grouped_heads_sampled():
+    # 64 heads x 64 query tiles: each XCD takes 8 heads in 4 groups of 2, rank-major inside
+    # a group; every head's rows are checked at sampled positions against the oracle
+    S, H, D = 8192, 64, 128
+    q, k, v = make_inputs(1, S, H, 8, D, seed=29)
+    qd, kd, vd = _to_dev(q, k, v)
+    o = torch.empty((1, S, H, D), device=dev())
+    lse = torch.empty((1, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd, vd, o, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()
+    worst_o = worst_l = 0.0
+    for h in range(H):
+        rows = sorted({0, S - 1, *(int(x) for x in rng.integers(0, S, 6))})
+        o_ref, l_ref = rows_forward(qn, kn, vn, 0, h, rows)
+        worst_o = max(worst_o, max_err(o[0, rows, h].cpu(), o_ref))
+        worst_l = max(worst_l, max_err(lse[0, h, rows].cpu(), l_ref))
+    log(f"grouped heads S={S} H={H}: O {worst_o:.3e} LSE {worst_l:.3e}")
+    assert worst_o <= TOL_O and worst_l <= TOL_LSE
 
 
 @pytest.mark.parametrize("n_chunks,S,B", [(8, 2048, 1), (3, 1000, 2)])
