@@ -150,6 +150,28 @@ def test_accumulate_late_chunk_ragged(B, S, k0):
     _check_pair(f"late chunk B={B} S={S} k0={k0}", o, lse, o_ref, l_ref, fin)
 
 
+@pytest.mark.parametrize("S,D", [(1000, 128), (333, 64)])
+def test_ring_accumulate_into_strided_outputs(S, D):
+    # a causal ring whose running output, LSE-paired bf16 result and the interleaved slices
+    # beside them share one packed buffer per dtype: the accumulate epilogue reads and
+    # writes its rows through o_stride (a ragged last tile included) and touches nothing else
+    H, n_chunks = 4, 3
+    q, k, v = make_inputs(1, S, H, H, D, seed=S + 7)
+    qd, kd, vd = _to_dev(q, k, v)
+    f32 = torch.full((1, S, 3, H, D), float("nan"), device=dev())
+    b16 = torch.full((1, S, 3, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
+    o_acc, out = f32[:, :, 1], b16[:, :, 1]
+    lse = torch.empty(1, H, S, device=dev())
+    order = chunk_order(n_chunks, seed=2)
+    ba.ring_forward(qd, kd, vd, n_chunks, order, o_acc=o_acc, lse=lse, out=out)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v))
+    _check_pair(f"strided ring S={S} D={D}", o_acc, lse, o_ref, l_ref, out)
+    assert torch.equal(out, o_acc.to(torch.bfloat16))
+    assert torch.isnan(f32[:, :, 0]).all() and torch.isnan(f32[:, :, 2]).all()
+    assert torch.isnan(b16[:, :, 0].float()).all() and torch.isnan(b16[:, :, 2].float()).all()
+
+
 def test_peaked_softmax():
     S, H, D = 1024, 2, 128
     q, k, v = make_inputs(1, S, H, H, D, seed=21, q_scale=4.0)
