@@ -12,7 +12,9 @@
 //     Summary);
 //  3. the backward over the same ring (delta on the first step, dQ accumulated
 //     in fp32 and converted on the last, dK and dV written per chunk) equals one
-//     backward call over all keys within a relative L2 of 1e-2 per gradient.
+//     backward call over all keys within a relative L2 of 1e-2 per gradient;
+//  4. the same backward ring through blockattn_bwd_noalloc (delta in the
+//     library's static buffer, recomputed on every call) gives the same bits.
 // Prints one line "abi_example ok ..." and exits 0, or prints the failure and
 // exits 1.
 #include <hip/hip_runtime_api.h>
@@ -229,9 +231,40 @@ int main() {
     fprintf(stderr, "backward ring vs one call: rel L2 dq %.3e dk %.3e dv %.3e\n", rel[0], rel[1], rel[2]);
     return fail("ring backward differs from the one-call backward");
   }
+  // ---- 4. the allocation-free entry point over the same ring: the same bits
+  void *dq3, *dk3, *dv3;
+  float* dqa3;
+  HIP_OK(hipMalloc(&dq3, n * 2));
+  HIP_OK(hipMalloc(&dk3, n * 2));
+  HIP_OK(hipMalloc(&dv3, n * 2));
+  HIP_OK(hipMalloc((void**)&dqa3, n * 4));
+  HIP_OK(hipMemset(dqa3, 0, n * 4));
+  for (int t = 0; t < n_chunks; ++t) {
+    ba_desc dc = d;
+    dc.seqlen_k = C;
+    dc.k_pos0 = order[t] * C;
+    const int64_t koff = dc.k_pos0 * strides[1] * 2;
+    const int flags = t == n_chunks - 1 ? BA_BWD_FINALIZE_DQ : 0;
+    const int st_ = blockattn_bwd_noalloc(&dc, q, (const char*)k + koff, (const char*)v + koff, o_bf16, dout,
+                                          lse_ring, dqa3, (char*)dk3 + koff, (char*)dv3 + koff, BA_BF16, dq3,
+                                          flags, st);
+    if (st_ != BA_OK) {
+      fprintf(stderr, "allocation-free backward ring step %d: %s\n", t, blockattn_status_string(st_));
+      return 1;
+    }
+  }
+  HIP_OK(hipStreamSynchronize(st));
+  void* const same[3][2] = {{dq2, dq3}, {dk2, dk3}, {dv2, dv3}};
+  for (int j = 0; j < 3; ++j) {
+    HIP_OK(hipMemcpy(ga.data(), same[j][0], n * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gb.data(), same[j][1], n * 2, hipMemcpyDeviceToHost));
+    if (memcmp(ga.data(), gb.data(), n * 2) != 0) return fail("the allocation-free backward differs from the ring");
+  }
+  hipFree(dq3); hipFree(dk3); hipFree(dv3); hipFree(dqa3);
+
   printf("abi_example ok: ring of %d chunks vs one call over S=%lld keys: max|dO| %.3e, max|dLSE| %.3e; "
-         "backward rel L2 dq %.3e dk %.3e dv %.3e; first output %.6f\n", (int)n_chunks, (long long)S, max_o,
-         max_l, rel[0], rel[1], rel[2], from_bf16(ob[0]));
+         "backward rel L2 dq %.3e dk %.3e dv %.3e; allocation-free backward bit-identical; first output %.6f\n",
+         (int)n_chunks, (long long)S, max_o, max_l, rel[0], rel[1], rel[2], from_bf16(ob[0]));
   hipFree(q); hipFree(k); hipFree(v); hipFree(o_ring); hipFree(o_one); hipFree(o_bf16);
   hipFree(lse_ring); hipFree(lse_one);
   hipFree(dout); hipFree(dq1); hipFree(dk1); hipFree(dv1); hipFree(dq2); hipFree(dk2); hipFree(dv2);
