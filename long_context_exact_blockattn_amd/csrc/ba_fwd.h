@@ -304,7 +304,6 @@ __global__ __launch_bounds__(kFwdThreads, 2 / kFwdQB) void fwd_kernel(FwdArgs a)
   // MFMA-layout accesses (32 rows, one piece each) spread over the banks; the direct loads
   // and the copy-out walk the stage linearly, 1 KB (whole rows) per instruction.
   static_assert(QB == 1, "the epilogue is written for one 32-row block per wave");
-  static_assert(32 * D * 4 <= TILE * 2 && 4 * NW == 16, "a wave's 32 fp32 rows must fit one of the four tile buffers");
   constexpr int SPR = D / 4;               // 16-byte pieces per staged row
   constexpr int NIO = 32 * SPR / 64;       // linear 1 KB steps per wave
   const float l_tot = halves_sum(l_run[0]);

@@ -19,6 +19,10 @@ namespace {
 
 using namespace ba;
 
+// the forward epilogue stages each wave's 32 fp32 rows in one of the four tile buffers
+static_assert(kFwdThreads == 256 && kFwdQB == 1 && 32 * 4 <= kFwdBN * 2,
+              "a wave's staged rows (32 x D fp32) must fit one tile buffer (BN x D bf16)");
+
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 int check_strides(const int64_t s[3]) {
