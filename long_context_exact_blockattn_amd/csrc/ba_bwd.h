@@ -99,7 +99,8 @@ struct TileLoader {
   }
 };
 static_assert(TileLoader<128, 64>::STEP % 16 == 0 && TileLoader<64, 64>::STEP % 16 == 0 &&
-                  TileLoader<128, 64, kKvThreads>::STEP % 16 == 0 && TileLoader<64, 64, kKvThreads>::STEP % 16 == 0,
+                  TileLoader<128, 64, kKvThreads / 2>::STEP % 16 == 0 &&
+                  TileLoader<64, 64, kKvThreads / 2>::STEP % 16 == 0,
               "the loader assumes the swizzle repeats every STEP rows");
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -347,7 +348,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 // tile buffers (tile j + 1 loads while tiles j - 1 and j are read) and two P
 // buffers.  Each wave keeps one stationary operand and one accumulator set,
 // so two waves fit on a SIMD and each one's VALU work runs under the other's
-// MFMAs.
+// MFMAs.  The P waves issue every tile load: both waves of a pair leave the
+// same barrier, and loads issued by both would hold both at issue while the
+// SIMD's matrix core idles.
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -413,7 +416,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       t_off[db][0] = tile_off<D>(r0, dcol);
       t_off[db][1] = tile_off<D>(r0 + 8, dcol);
     }
-    TileLoader<D, BM, kKvThreads> ld;
+    // only the four P waves load tiles (8 direct loads each per tile): a burst of loads
+    // holds its wave at issue for hundreds of cycles, and the P wave, with the lighter
+    // phases, has that slack while its dS partner on the same SIMD goes on with its MFMAs
+    TileLoader<D, BM, kKvThreads / 2> ld;
     ld.init(wave, lane);
     const int qs_s = (int)a.qs_s;
     const int os_s = (int)a.os_s;
@@ -446,8 +452,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
       const int64_t qbase = (int64_t)b * a.qs_b + t.row0 * a.qs_s + (int64_t)hh * a.qs_h;
       const int64_t obase = (int64_t)b * a.os_b + t.row0 * a.os_s + (int64_t)hh * a.os_h;
-      ld.issue(a.q + qbase, qs_s, (int)t.rows, qd, wave);
-      ld.issue(a.dout + obase, os_s, (int)t.rows, qd + TILE, wave);
+      if (pwave) {
+        ld.issue(a.q + qbase, qs_s, (int)t.rows, qd, wave);
+        ld.issue(a.dout + obase, os_s, (int)t.rows, qd + TILE, wave);
+      }
     };
     auto put_stats = [&](int buf) {
       if (tid < BM) {
@@ -587,13 +595,14 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    // interval j (0 <= j <= n_iter): load tile j + 1 into Tl, phase 2 of tile
-    // j - 1 (buffer Tp), phase 1 of tile j (buffer Tc); buffer and statistics
-    // slots rotate with j mod 3, P slots with j mod 2
+    // interval j (0 <= j <= n_iter): phase 2 of tile j - 1 (buffer Tp), the loads of
+    // tile j + 1 into Tl (issued after phase 2, when the dS waves are deep in their
+    // heavier phase 2), phase 1 of tile j (buffer Tc); buffer and statistics slots
+    // rotate with j mod 3, P slots with j mod 2
     auto interval = [&](bf16* Tc, const bf16* Tp, bf16* Tl, int64_t j, int rot) __attribute__((always_inline)) {
       const int par = (int)(j & 1);
-      if (j + 1 < n_iter) issue(Tl);
       if (j >= 1) phase2(Tp, rot == 0 ? 2 : rot - 1, par ^ 1);
+      if (j + 1 < n_iter) issue(Tl);
       // x and pf are rewritten by phase 1: keep the two phases apart
       __builtin_amdgcn_sched_barrier(0);
       if (j < n_iter) phase1(Tc, rot, par);
