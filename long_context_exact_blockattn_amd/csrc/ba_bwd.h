@@ -53,6 +53,7 @@ struct BwdArgs {
 };
 
 constexpr int kDqBM = 128;   // query rows per dq item (4 waves x 32)
+constexpr int kDqSlotsPerXcd = 64;  // two dq workgroups per CU, 32 CUs per XCD
 constexpr int kDqBN = 64;    // key rows per streamed tile
 constexpr int kKvBN = 128;   // keys per dkdv item (4 waves x 32)
 constexpr int kKvBM = 64;    // query rows per streamed tile

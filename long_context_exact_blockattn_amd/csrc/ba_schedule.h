@@ -183,12 +183,12 @@ BA_HD void qitem_of_pid(int64_t pid, int64_t n_ranks, int64_t hx, int64_t& bh, i
 }
 
 // Group size hx for qitem_of_pid, or 0 for head-major order: enough heads for two
-// rounds of an XCD's 64 workgroup slots (256 CUs in 8 XCDs, two workgroups each),
-// a divisor of the heads each XCD takes.
-inline int64_t interleave_heads(int64_t n_bh, int64_t n_ranks) {
-  if (n_ranks <= 0 || n_ranks >= 128 || n_bh % 8 != 0) return 0;
+// rounds of an XCD's workgroup slots (256 CUs in 8 XCDs; slots = workgroups an XCD
+// runs at once), a divisor of the heads each XCD takes.
+inline int64_t interleave_heads(int64_t n_bh, int64_t n_ranks, int64_t slots) {
+  if (n_ranks <= 0 || n_ranks >= 2 * slots || n_bh % 8 != 0) return 0;
   const int64_t per_xcd = n_bh / 8;
-  int64_t g = (128 + n_ranks - 1) / n_ranks;
+  int64_t g = (2 * slots + n_ranks - 1) / n_ranks;
   if (g > per_xcd) g = per_xcd;
   while (per_xcd % g != 0) --g;
   return g;

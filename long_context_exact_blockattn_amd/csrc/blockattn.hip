@@ -19,8 +19,8 @@ namespace {
 
 using namespace ba;
 
-// the forward epilogue stages each wave's 32 fp32 rows in one of the four tile buffers
-static_assert(kFwdThreads == 256 && kFwdQB == 1 && 32 * 4 <= kFwdBN * 2,
+// the forward epilogue stages each wave's 32 fp32 rows in one of its eight tile-sized arrays
+static_assert(kFwdWaves == 8 && kFwdBM == 32 * kFwdWaves && 32 * 4 <= kFwdBN * 2,
               "a wave's staged rows (32 x D fp32) must fit one tile buffer (BN x D bf16)");
 
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
@@ -119,7 +119,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   }
   a.n_ranks = a.n_qtiles - skip_qt;
   a.n_items = (int64_t)d->batch * d->heads_q * a.n_ranks;
-  a.hx = interleave_heads((int64_t)d->batch * d->heads_q, a.n_ranks);
+  a.hx = interleave_heads((int64_t)d->batch * d->heads_q, a.n_ranks, kFwdSlotsPerXcd);
   if (a.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
   if (o_final && skip_qt > 0) {
     StoreArgs st;
@@ -217,7 +217,7 @@ int bwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
     }
     b.n_ranks = b.n_tiles - skip_qt;
     b.n_items = (int64_t)d->batch * d->heads_q * b.n_ranks;
-    b.hx = interleave_heads((int64_t)d->batch * d->heads_q, b.n_ranks);
+    b.hx = interleave_heads((int64_t)d->batch * d->heads_q, b.n_ranks, kDqSlotsPerXcd);
     if (b.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
     if (finalize && skip_qt > 0) {
       StoreArgs st;
