@@ -103,7 +103,7 @@ typedef struct {
  * their original rows; heads [0, shift_head0) attend causally inside groups of
  * original positions.  Requirements (else BA_ERR_S2): seqlen_q == seqlen_k = S,
  * q_pos0 == k_pos0 == 0, causal == 1, group even, S % group == 0,
- * (group / 2) % 128 == 0 (a tile never straddles the roll), 0 <= shift_head0
+ * (group / 2) % 256 == 0 (a query tile never straddles the roll), 0 <= shift_head0
  * <= Hq and shift_head0 % (Hq / Hkv) == 0 (a key/value head is either shifted
  * for all of its query heads or for none). */
 typedef struct {

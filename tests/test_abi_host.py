@@ -105,6 +105,7 @@ def test_merge_and_s2_validation(lib):
     assert lib.s2attn_fwd(ctypes.byref(d), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0, P(FAKE), None) == _lib.BA_ERR_NULL
     assert s2(_desc(Sq=1024, Sk=1024), 300, 1) == _lib.BA_ERR_S2       # group does not divide S
     assert s2(_desc(Sq=1024, Sk=1024), 128, 1) == _lib.BA_ERR_S2       # group/2 not a tile multiple
+    assert s2(_desc(Sq=1024, Sk=1024), 256, 1) == _lib.BA_ERR_S2       # group/2 = 128: half a 256-row query tile
     assert s2(_desc(Sq=1024, Sk=512), 256, 1) == _lib.BA_ERR_S2        # Sq != Sk
     assert s2(_desc(Sq=1024, Sk=1024, k0=256), 256, 1) == _lib.BA_ERR_S2
     assert s2(_desc(Sq=1024, Sk=1024, Hq=8, Hkv=2), 256, 3) == _lib.BA_ERR_S2  # shift boundary inside a KV group
