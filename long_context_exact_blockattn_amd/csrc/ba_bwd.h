@@ -339,7 +339,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 // share a SIMD.  The P wave holds K and computes S, P = exp(S - LSE) and
 // dV += P^T dO; the dS wave holds V and computes dP = dO V^T, dS = P (dP -
 // delta) and dK += dS^T Q, taking P from the P wave through LDS (bf16, in the
-// accumulator layout both waves share: lane = key, register = query).  Each
+// accumulator layout both waves share: lane = key, register = query).  The dS
+// wave's dP accumulator starts at -delta, so its MFMAs leave dP - delta and dS
+// costs one product per element.  Each
 // tile of 64 query rows has two phases per wave: the score / dP MFMAs (with
 // the softmax on the P wave), then the two gradient contractions.  The phases
 // are skewed by one tile: between two barriers every wave runs phase 2 of
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // arrays so prefetches into one buffer do not make the compiler wait before
   // reading the others
   __shared__ __attribute__((aligned(16))) bf16 sT0[2 * TILE], sT1[2 * TILE], sT2[2 * TILE];
-  __shared__ __attribute__((aligned(16))) float stat[3][2][BM];  // [buffer][lse*log2e, delta][row]
+  __shared__ __attribute__((aligned(16))) float stat[3][2][BM];  // [buffer][lse*log2e, -delta][row]
   __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][NKB][2][2][64];  // [parity][key block][qb][half][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     auto put_stats = [&](int buf) {
       if (tid < BM) {
         stat[buf][0][tid] = st_ok ? st_l * kLog2e : INFINITY;
-        stat[buf][1][tid] = st_ok ? st_d : 0.f;
+        stat[buf][1][tid] = st_ok ? -st_d : 0.f;
       }
     };
 
@@ -479,6 +481,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) act[qb] = !(a.causal && wave_kmin > t.cpos0 + qb * 32 + 31);
       const float* lse_s = stat[sbuf][0];
+      const float* ndel_s = stat[sbuf][1];
       const bf16* Xs = QDs + (pwave ? 0 : TILE);
       auto contract = [&](int qb) __attribute__((always_inline)) {
         bf16x8 fr[2][2];
@@ -486,11 +489,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           fr[set][0] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2]);
           fr[set][1] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2 + 1]);
         };
+        // the dS wave's dP^T accumulator starts at -delta (each register's query row, the
+        // same in every key lane), so that its MFMAs leave dP - delta
+        f32x16 init = f32x16{};
+        if (!pwave) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *(const f32x4*)(ndel_s + qb * 32 + 8 * g + 4 * hl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) init[4 * g + e] = d4[e];
+          }
+        }
         rd(0, 0);
 #pragma unroll
         for (int kk2 = 0; kk2 < KK / 2; ++kk2) {
           if (kk2 + 1 < KK / 2) rd(kk2 + 1, (kk2 + 1) & 1);
-          x[qb] = mfma32(fr[kk2 & 1][0], sf[2 * kk2], kk2 == 0 ? f32x16{} : x[qb]);
+          x[qb] = mfma32(fr[kk2 & 1][0], sf[2 * kk2], kk2 == 0 ? init : x[qb]);
           x[qb] = mfma32(fr[kk2 & 1][1], sf[2 * kk2 + 1], x[qb]);
         }
       };
@@ -554,43 +568,43 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
     // ---- phase 2: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
     // transposed operand is read from the [query][d] tile
-    auto phase2 = [&](const bf16* QDs, int sbuf, int par) __attribute__((always_inline)) {
-      const float* del_s = stat[sbuf][1];
+    auto phase2 = [&](const bf16* QDs, int par) __attribute__((always_inline)) {
       const bf16* Ys = QDs + (pwave ? TILE : 0);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         if (!act[qb]) continue;
+        // transposed fragments read two MFMAs ahead of their use; the first two are issued
+        // with the P reads, before the dS wave's vector work
+        bf16x8 tf[3];
+        auto rdt = [&](int j) __attribute__((always_inline)) {
+          const int db = j >> 1, c2 = j & 1;
+          tf[j % 3] = tr_pair(Ys + (qb * 32 + 16 * c2) * D, t_off[db][0], t_off[db][1]);
+        };
         bf16x8 yf[2];
         if (pwave) {
           // its own P, back from LDS: no registers held across the barrier
           yf[0] = pbuf[par][kblk][qb][0][lane];
           yf[1] = pbuf[par][kblk][qb][1][lane];
+          rdt(0);
+          rdt(1);
         } else {
           const bf16x8 p0 = pbuf[par][kblk][qb][0][lane];
           const bf16x8 p1 = pbuf[par][kblk][qb][1][lane];
+          rdt(0);
+          rdt(1);
+          __builtin_amdgcn_sched_barrier(0);
+          // dS = P (dP - delta); x already holds dP - delta
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 d4 = *(const f32x4*)(del_s + qb * 32 + 8 * g + 4 * hl);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
-              yf[r >> 3][r & 7] = (bf16)(p * (x[qb][r] - d4[e]));
-            }
+          for (int r = 0; r < 16; ++r) {
+            const float p = (float)(r < 8 ? p0[r & 7] : p1[r & 7]);
+            yf[r >> 3][r & 7] = (bf16)(p * x[qb][r]);
           }
         }
-        // transposed fragments read one step ahead of their MFMAs
-        bf16x8 tf[2];
-        auto rdt = [&](int j) __attribute__((always_inline)) {
-          const int db = j >> 1, c2 = j & 1;
-          tf[j & 1] = tr_pair(Ys + (qb * 32 + 16 * c2) * D, t_off[db][0], t_off[db][1]);
-        };
-        rdt(0);
 #pragma unroll
         for (int j = 0; j < 2 * DB; ++j) {
-          if (j + 1 < 2 * DB) rdt(j + 1);
+          if (j + 2 < 2 * DB) rdt(j + 2);
           __builtin_amdgcn_sched_barrier(0);
-          acc[j >> 1] = mfma32(tf[j & 1], yf[j & 1], acc[j >> 1]);
+          acc[j >> 1] = mfma32(tf[j % 3], yf[j & 1], acc[j >> 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -602,7 +616,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // rotate with j mod 3, P slots with j mod 2
     auto interval = [&](bf16* Tc, const bf16* Tp, bf16* Tl, int64_t j, int rot) __attribute__((always_inline)) {
       const int par = (int)(j & 1);
-      if (j >= 1) phase2(Tp, rot == 0 ? 2 : rot - 1, par ^ 1);
+      if (j >= 1) phase2(Tp, par ^ 1);
       if (j + 1 < n_iter) issue(Tl);
       // x and pf are rewritten by phase 1: keep the two phases apart
       __builtin_amdgcn_sched_barrier(0);
