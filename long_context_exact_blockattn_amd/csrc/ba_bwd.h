@@ -244,14 +244,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       };
       // dQ^T += K^T dS^T: K^T operand read transposed from the [key][d] tile
-      auto accumulate = [&](int kb) __attribute__((always_inline)) {
+      // (strict: the reads stay two MFMAs ahead; not where another block's vector work is
+      // interleaved with these MFMAs)
+      auto accumulate = [&](int kb, bool strict) __attribute__((always_inline)) {
+        bf16x8 tf[3];
+        auto rdt = [&](int j) __attribute__((always_inline)) {
+          const int db = j >> 1, c2 = j & 1;
+          tf[j % 3] = tr_pair(Ks + (kb * 32 + 16 * c2) * D, t_off[db][0], t_off[db][1]);
+        };
+        rdt(0);
+        rdt(1);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const bf16* base = Ks + (kb * 32 + 16 * c2) * D;
-            dqacc[db] = mfma32(tr_pair(base, t_off[db][0], t_off[db][1]), dsf[kb][c2], dqacc[db]);
-          }
+        for (int j = 0; j < 2 * DB; ++j) {
+          if (j + 2 < 2 * DB) rdt(j + 2);
+          if (strict) __builtin_amdgcn_sched_barrier(0);
+          dqacc[j >> 1] = mfma32(tf[j % 3], dsf[kb][j & 1], dqacc[j >> 1]);
+          if (strict) __builtin_amdgcn_sched_barrier(0);
+        }
       };
       if (!need_mask) {
         // common case, straight-line: each 32-key block's vector work runs between the
@@ -265,20 +274,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU
         }
         __builtin_amdgcn_sched_barrier(0);
-        accumulate(0);
+        accumulate(0, false);
         make_ds(1, false);
         for (int j = 0; j < 2 * DB; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           __builtin_amdgcn_sched_group_barrier(0x402, 8, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        accumulate(1);
+        accumulate(1, true);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           scores(kb);
           make_ds(kb, true);
-          accumulate(kb);
+          accumulate(kb, true);
         }
       }
     };
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const float* lse_s = stat[sbuf][0];
       const float* ndel_s = stat[sbuf][1];
       const bf16* Xs = QDs + (pwave ? 0 : TILE);
-      auto contract = [&](int qb) __attribute__((always_inline)) {
+      auto contract = [&](int qb, bool strict) __attribute__((always_inline)) {
         bf16x8 fr[2][2];
         auto rd = [&](int kk2, int set) __attribute__((always_inline)) {
           fr[set][0] = *(const bf16x8*)(Xs + qb * 32 * D + n_off[2 * kk2]);
@@ -504,8 +513,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int kk2 = 0; kk2 < KK / 2; ++kk2) {
           if (kk2 + 1 < KK / 2) rd(kk2 + 1, (kk2 + 1) & 1);
+          // strict: each pair's reads stay ahead of the MFMAs (left to itself the scheduler
+          // reuses one register quad and waits on every read); not where another block's
+          // vector work is interleaved with these MFMAs
+          if (strict) __builtin_amdgcn_sched_barrier(0);
           x[qb] = mfma32(fr[kk2 & 1][0], sf[2 * kk2], kk2 == 0 ? init : x[qb]);
           x[qb] = mfma32(fr[kk2 & 1][1], sf[2 * kk2 + 1], x[qb]);
+          if (strict) __builtin_amdgcn_sched_barrier(0);
         }
       };
       // P = exp(S - LSE) of block qb (zero where masked), in bf16 to LDS for both
@@ -544,9 +558,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if (pwave && act[0] && act[1] && !need_mask_of(0)) {
         // common case, straight-line: block 1's score MFMAs interleaved with block 0's
         // softmax so that the wave's vector work runs under its own matrix work
-        contract(0);
+        contract(0, true);
         __builtin_amdgcn_sched_barrier(0);
-        contract(1);
+        contract(1, false);
         softmax(0, false);
         for (int j = 0; j < KK; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -557,7 +571,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       } else {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          if (act[qb]) contract(qb);
+          if (act[qb]) contract(qb, true);
         if (pwave) {
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
