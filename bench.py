@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import sys
 import time
@@ -216,7 +217,45 @@ def side_measurements(w, tensors, reps=5):
                               "overhead_pct": round(100 * (ms_staged / ms_plain - 1), 2),
                               "copy_bytes_per_step": chunk_bytes,
                               "copy_alone_ms_per_step": round(ms_copy / w.n_chunks, 4)}
+    res["dense_gemm"] = dense_gemm_context()
     return res
+
+
+def ring_step_table(w, launch_ms, order, one_shot_ms):
+    """Per ring position: the chunk, its median launch time (the last position includes the bf16
+    store of the rows its chunk cannot reach), its allowed (query, key) pairs, TFLOP/s, and its time
+    over its pair share of the one-call forward: where the ring's cost over one call sits."""
+    from workloads import chunk_bounds
+    bounds = chunk_bounds(w.seqlen, w.n_chunks)
+    n = len(order)
+    total = w.allowed_pairs_per_head()
+    rows = []
+    for t, c in enumerate(order):
+        c0, c1 = bounds[c]
+        ln = c1 - c0
+        pairs = ln * (ln + 1) // 2 + (w.seqlen - c1) * ln  # causal: the chunk's own block, then full rows
+        ms = statistics.median(launch_ms[t::n])
+        flop = 4.0 * w.batch * w.heads_q * w.head_dim * pairs
+        rows.append({"pos": t, "chunk": c, "ms": round(ms, 4), "tflops": round(flop / ms / 1e9, 1),
+                     "over_share": round(ms / (one_shot_ms * pairs / total), 3)})
+    return rows
+
+
+def dense_gemm_context(n=8192, reps=20):
+    """Context for the MFMA roofline, not a kernel of the path: a square bf16 GEMM through torch
+    (the vendor BLAS) at n, timed with events, as TFLOP/s and as a fraction of the nominal peak.
+    It shows what a dense contraction sustains on this chip at the engine clock its power allows."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    ms = _event_ms(lambda: torch.mm(a, b, out=c), reps)
+    tf = 2.0 * n ** 3 / ms / 1e9
+    return {"shape": [n, n, n], "dtype": "bf16", "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "via": "torch.mm (vendor BLAS)"}
 
 
 def run_training(w, steps, warmup, tensors=None, one_shot=True):
@@ -907,7 +946,9 @@ def main():
         side = side_measurements(w, tensors)
         line["one_shot"] = dict(side["one_shot"],
                                 ring_overhead_pct=round(100 * (ms_per_step / side["one_shot"]["ms"] - 1), 2))
+        line["ring_steps"] = ring_step_table(w, r["launch_ms"], r["order"], side["one_shot"]["ms"])
         line["hbm_kernels"] = side["hbm_kernels"]
+        line["dense_gemm"] = side["dense_gemm"]
         if "ring_staged" in side:
             line["ring_staged"] = side["ring_staged"]
     if not args.no_cpu_baseline:

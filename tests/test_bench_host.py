@@ -180,3 +180,22 @@ def test_counter_table_normalises_per_cu_cycle(tmp_path, capsys):
     assert "1 dispatches of fwd_kernel<128>" in out
     assert "LDS busy 0.250 of cycles; LDS loads 64.0 B per CU-cycle" in out
     assert "MFMA busy 0.500 of SIMD-cycles" in out and "in 0.100 of SIMD-cycles" in out
+
+
+def test_ring_step_table_splits_the_causal_pairs():
+    """The per-position pair counts of a causal ring add up to the workload's allowed pairs, so a
+    ring whose launches each take their pair share of the one-call time reads 1.0 everywhere."""
+    from workloads import chunk_order, get
+    w = get("llama2_7b_s32k_ring8")
+    order = chunk_order(w.n_chunks, seed=w.seed)
+    one_shot_ms = 8.0
+    # launch times exactly proportional to each chunk's pairs, two timed steps
+    L = w.chunk_len
+    pairs = [L * (L + 1) // 2 + (w.seqlen - (c + 1) * L) * L for c in order]
+    assert sum(pairs) == w.allowed_pairs_per_head()
+    ms = [one_shot_ms * p / w.allowed_pairs_per_head() for p in pairs]
+    rows = bench.ring_step_table(w, ms + ms, order, one_shot_ms)
+    assert [r["chunk"] for r in rows] == order
+    assert all(abs(r["over_share"] - 1.0) < 1e-3 for r in rows)
+    flop = sum(r["tflops"] * r["ms"] * 1e9 for r in rows)
+    assert abs(flop / w.fwd_flop() - 1.0) < 1e-3
