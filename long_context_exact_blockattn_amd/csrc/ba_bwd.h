@@ -234,12 +234,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
           dp[kb] = mfma32(*(const bf16x8*)(Vs + kb * 32 * D + n_off[kk]), df[kk], kk == 0 ? f32x16{} : dp[kb]);
         }
       };
-      auto make_ds = [&](int kb, bool masked) __attribute__((always_inline)) {
+      // keys past the tile's valid rows or (causal) after this lane's row get a score of
+      // -inf, so that P = 0 there: only the scores branch on the mask, and both kinds of
+      // tile share one MFMA schedule (with two paths, the compiler copies the whole dQ
+      // accumulator to merge them)
+      auto mask = [&](int kb) __attribute__((always_inline)) {
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            s[kb][r] = key <= lim ? s[kb][r] : -INFINITY;
+          }
+        }
+      };
+      auto make_ds = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2));
-          if (masked) p = key <= lim ? p : 0.f;
+          const float p = exp2_hw(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2));
           dsf[kb][r >> 3][r & 7] = (bf16)(p * (dp[kb][r] - dlt));
         }
       };
@@ -262,34 +273,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
           if (strict) __builtin_amdgcn_sched_barrier(0);
         }
       };
-      if (!need_mask) {
-        // common case, straight-line: each 32-key block's vector work runs between the
-        // MFMAs of the next step (block 1's scores, then block 0's dQ)
-        scores(0);
-        __builtin_amdgcn_sched_barrier(0);
-        scores(1);
-        make_ds(0, false);
-        for (int j = 0; j < 2 * KK; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        accumulate(0, false);
-        make_ds(1, false);
-        for (int j = 0; j < 2 * DB; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(0x402, 8, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        accumulate(1, true);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          scores(kb);
-          make_ds(kb, true);
-          accumulate(kb, true);
-        }
+      // each 32-key block's vector work runs between the MFMAs of the next step (block 1's
+      // scores, then block 0's dQ)
+      scores(0);
+      __builtin_amdgcn_sched_barrier(0);
+      mask(0);
+      __builtin_amdgcn_sched_barrier(0);
+      scores(1);
+      make_ds(0);
+      for (int j = 0; j < 2 * KK; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU
       }
+      __builtin_amdgcn_sched_barrier(0);
+      mask(1);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(0, false);
+      make_ds(1);
+      for (int j = 0; j < 2 * DB; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x402, 8, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(1, true);
     };
 
     bf16* K0 = smem;

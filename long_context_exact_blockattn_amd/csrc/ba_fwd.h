@@ -234,8 +234,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       }
     };
 
-    // ---- online softmax (base 2): scores -> P, running max / sum, rare O rescale
-    auto softmax = [&]() __attribute__((always_inline)) {
+    // ---- online softmax (base 2): scores -> P, running max / sum, rare O rescale.  With
+    // DEFER (group A, whose P V of this tile comes after the next barrier) the rescale of O is
+    // left to the start of that P V phase, right before the MFMAs that accumulate into O: at
+    // the end of the softmax, the compiler merged the rescaled and the untouched accumulator
+    // by copying all 64 of its registers out and back on every tile.
+    float al_pend = 1.f;  // pending O factor (DEFER), per lane; 1 where the max did not move
+    bool resc_pend = false;  // whether any lane of the wave has a pending factor (uniform)
+    auto softmax = [&](auto defer) __attribute__((always_inline)) {
+      constexpr bool DEFER = decltype(defer)::value;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -264,8 +271,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       if (__any(m_new != m_old)) {
         const float al = exp2_hw(m_old - m_use);
         l_run = l_run * al + rsum;
+        if (DEFER) {
+          al_pend = al;
+          resc_pend = true;
+        } else {
 #pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= al;
+          for (int i = 0; i < DB; ++i) oacc[i] *= al;
+        }
       } else {
         l_run = l_run + rsum;
       }
@@ -274,6 +286,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
 
     // ---- O^T += V^T P^T ; V^T operand read transposed from the [key][d] tile
     auto pv = [&](const bf16* Vs) __attribute__((always_inline)) {
+      if (resc_pend) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[i] *= al_pend;
+        resc_pend = false;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -303,12 +320,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
             scores(Kc);
             __builtin_amdgcn_sched_barrier(0);
             mask(kt0 + j);
-            softmax();
+            softmax(std::true_type{});
           }
         } else {
           if (prev) {
             mask(kt0 + j - 1);
-            softmax();
+            softmax(std::false_type{});
             // the softmax stays pure vector work: an MFMA issued among it would stall the
             // rest of it while the other group's MFMAs hold the matrix core
             __builtin_amdgcn_sched_barrier(0);
