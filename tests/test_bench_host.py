@@ -50,12 +50,14 @@ def test_trace_summary_averages_per_kernel(tmp_path, capsys):
     assert lines[1].split()[:4] == ["1", "calls", "avg", "0.500"]
 
 
-def _counters_db(path, rows):
+def _counters_db(path, rows, duration_ns=1000):
+    """rocprofv3's counters_collection table, each dispatch lasting duration_ns."""
     os.makedirs(os.path.dirname(path), exist_ok=True)
     con = sqlite3.connect(path)
     con.execute("create table counters_collection (dispatch_id integer, kernel_name text, counter_name text, "
-                "value real)")
-    con.executemany("insert into counters_collection values (?, ?, ?, ?)", rows)
+                "value real, duration integer)")
+    con.executemany("insert into counters_collection values (?, ?, ?, ?, ?)",
+                    [(*r, duration_ns) for r in rows])
     con.commit()
     con.close()
 
@@ -159,6 +161,8 @@ def test_counter_summary_of_another_kernel_prints_only(tmp_path, capsys):
     assert "1 dispatches of bwd_dkdv_kernel<128>" in text
     # 500 busy cycles per SIMD over 1000 cycles; 1.9 LDS instructions per MFMA
     assert "mfma_busy          0.500" in text and "lds_per_mfma       1.900" in text
+    # 8000 GRBM counts over 8 XCDs = 1000 cycles in the dispatch's 1000 ns: 1 GHz
+    assert "engine_clock_ghz    1.000" in text
     assert not os.path.exists(out)  # the summary record is the forward's only
 
 
