@@ -211,12 +211,34 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       ld.issue(vbase + t.row0 * a.ks_s, ks_s, (int)t.rows, vd, wave);
     };
 
-    auto tile_step = [&](const bf16* Ks, const bf16* Vs, int64_t kt) {
-      const KTile t = make_ktile(sc, kt);
-      if (a.causal && t.cpos0 > wave_cmax) return;  // every key after every row of this wave
-      const bool need_mask = (t.rows < BN) || (a.causal && t.cpos0 + BN - 1 > wave_cmin);
+    // Per-wave tile thresholds, once per item, relative to the item's first key tile (32-bit
+    // scalar compares per tile; 64-bit signed compares go to the vector ALU): the key
+    // coordinate of tile kt is c0 + kt*BN (make_ktile), so from act_end on every key of a tile
+    // comes after every row of this wave (causal), and from mask_from on a tile needs the mask
+    // (causal diagonal, or the chunk's ragged last tile).
+    constexpr int LBN = __builtin_ctz(BN);
+    static_assert((1 << LBN) == BN, "floor division by BN as a shift");
+    const int64_t kt_b = qt.kt_begin;
+    const int T = (int)(qt.kt_end - qt.kt_begin);
+    const int64_t c0 = a.s2_group > 0 ? 0 : a.k_pos0;
+    const int64_t act_end = a.causal ? ((wave_cmax - c0) >> LBN) + 1 : INT64_MAX;
+    int64_t mask_from = a.causal ? ((wave_cmin - c0 + 1) >> LBN) : INT64_MAX;
+    if (a.s2_group == 0 && a.Sk % BN != 0) {
+      const int64_t last = ceil_div(a.Sk, BN) - 1;
+      mask_from = last < mask_from ? last : mask_from;
+    }
+    auto rel = [&](int64_t kt) {
+      const int64_t r = kt - kt_b;
+      return (int)(r < 0 ? 0 : (r > T + 1 ? T + 1 : r));
+    };
+    const int act_rel = rel(act_end), mask_rel = rel(mask_from);
+
+    auto tile_step = [&](const bf16* Ks, const bf16* Vs, int j) {
+      if (j >= act_rel) return;  // every key after every row of this wave
+      const bool need_mask = j >= mask_rel;
       int lim = BN;
       if (need_mask) {
+        const KTile t = make_ktile(sc, kt_b + j);
         lim = (int)t.rows - 1;
         if (a.causal) {
           int64_t c = wave_cmin - t.cpos0;
@@ -302,17 +324,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     bf16* V0 = smem + TILE;
     bf16* K1 = smem + 2 * TILE;
     bf16* V1 = smem + 3 * TILE;
-    issue(K0, V0, qt.kt_begin);
+    issue(K0, V0, kt_b);
     wait_vmem();
     __syncthreads();
-    for (int64_t kt = qt.kt_begin; kt < qt.kt_end; kt += 2) {
-      if (kt + 1 < qt.kt_end) issue(K1, V1, kt + 1);
-      tile_step(K0, V0, kt);
+    for (int j = 0; j < T; j += 2) {
+      if (j + 1 < T) issue(K1, V1, kt_b + j + 1);
+      tile_step(K0, V0, j);
       wait_vmem();
       __syncthreads();
-      if (kt + 1 >= qt.kt_end) break;
-      if (kt + 2 < qt.kt_end) issue(K0, V0, kt + 2);
-      tile_step(K1, V1, kt + 1);
+      if (j + 1 >= T) break;
+      if (j + 2 < T) issue(K0, V0, kt_b + j + 2);
+      tile_step(K1, V1, j + 1);
       wait_vmem();
       __syncthreads();
     }
@@ -420,7 +442,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   const int64_t nqt = it.qt_end > it.qt_begin ? it.qt_end - it.qt_begin : 0;
-  const int64_t n_iter = nqt * a.grp;
+  const int n_iter = (int)(nqt * a.grp);  // query tiles x heads of the group (32-bit loop control)
   if (n_iter > 0) {
     int n_off[KK];
 #pragma unroll
@@ -634,7 +656,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // tile j + 1 into Tl (issued after phase 2, when the dS waves are deep in their
     // heavier phase 2), phase 1 of tile j (buffer Tc); buffer and statistics slots
     // rotate with j mod 3, P slots with j mod 2
-    auto interval = [&](bf16* Tc, const bf16* Tp, bf16* Tl, int64_t j, int rot) __attribute__((always_inline)) {
+    auto interval = [&](bf16* Tc, const bf16* Tp, bf16* Tl, int j, int rot) __attribute__((always_inline)) {
       const int par = (int)(j & 1);
       if (j >= 1) phase2(Tp, par ^ 1);
       if (j + 1 < n_iter) issue(Tl);
@@ -651,7 +673,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     // unrolled by three so that every buffer sits at a fixed LDS address
-    for (int64_t j = 0;; j += 3) {
+    for (int j = 0;; j += 3) {
       interval(sT0, sT2, sT1, j, 0);
       if (j + 1 > n_iter) break;
       interval(sT1, sT0, sT2, j + 1, 1);

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
     // Per-wave tile thresholds, once per item: the key coordinate of tile kt is c0 + kt*BN
     // (make_ktile), so from act_end on no key of a tile is allowed for any row of this wave
     // (causal) and from mask_from on a tile needs the mask (causal diagonal, or the chunk's
-    // ragged last tile).  Per interval the tests are then two scalar compares.
+    // ragged last tile).  Per interval the tests are then two scalar compares, in 32 bits
+    // relative to the item's first tile (64-bit signed compares go to the vector ALU).
     constexpr int LBN = __builtin_ctz(BN);
     static_assert((1 << LBN) == BN, "floor division by BN as a shift");
     const int64_t c0 = a.s2_group > 0 ? 0 : a.k_pos0;
@@ -180,8 +181,16 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       const int64_t last = ceil_div(a.Sk, BN) - 1;
       mask_from = last < mask_from ? last : mask_from;
     }
-    // whether this wave has any allowed key in tile kt (causal: not every key after every row)
-    auto active = [&](int64_t kt) __attribute__((always_inline)) { return kt < act_end; };
+    // Intervals j = 0 .. T (T = the item's key tiles); tile j is tile kt_begin + j
+    const int64_t kt0 = qt.kt_begin;
+    const int T = (int)(qt.kt_end - qt.kt_begin);
+    auto rel = [&](int64_t kt) __attribute__((always_inline)) {
+      const int64_t r = kt - kt0;
+      return (int)(r < 0 ? 0 : (r > T + 1 ? T + 1 : r));
+    };
+    const int act_rel = rel(act_end), mask_rel = rel(mask_from);
+    // whether this wave has any allowed key in tile j (causal: not every key after every row)
+    auto active = [&](int j) __attribute__((always_inline)) { return j < act_rel; };
 
     f32x16 s[2];   // S^T of the wave's 32 rows x the tile's two 32-key blocks
     bf16x8 pf[4];  // P in bf16, B operand of the P V MFMAs (k-step kc = keys 16kc..16kc+15)
@@ -212,10 +221,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       }
     };
 
-    // ---- mask of tile kt: keys past the chunk's end or (causal) after this lane's row
-    auto mask = [&](int64_t kt) __attribute__((always_inline)) {
-      if (kt >= mask_from) {
-        const KTile t = make_ktile(sc, kt);
+    // ---- mask of tile j: keys past the chunk's end or (causal) after this lane's row
+    auto mask = [&](int j) __attribute__((always_inline)) {
+      if (j >= mask_rel) {
+        const KTile t = make_ktile(sc, kt0 + j);
         // last allowed key index of this lane's row, in 32 bits
         int lim = (int)t.rows - 1;
         if (a.causal) {
@@ -303,28 +312,25 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
       }
     };
 
-    // Intervals j = 0 .. T (T = the item's key tiles); tile j is tile kt_begin + j.  Each
-    // group runs its own copy of the loop, so what one group keeps across a barrier (P for
-    // A, the scores for B) is not live in the other's.  Both copies pass the same barriers.
-    const int64_t kt0 = qt.kt_begin;
-    const int64_t T = qt.kt_end - qt.kt_begin;
+    // Each group runs its own copy of the loop, so what one group keeps across a barrier (P
+    // for A, the scores for B) is not live in the other's.  Both copies pass the same barriers.
     auto run = [&](auto group_b) __attribute__((always_inline)) {
       constexpr bool GB = decltype(group_b)::value;
-      auto interval = [&](int64_t j, const bf16* Kc, const bf16* Vp, bf16* Kn, bf16* Vn) __attribute__((always_inline)) {
+      auto interval = [&](int j, const bf16* Kc, const bf16* Vp, bf16* Kn, bf16* Vn) __attribute__((always_inline)) {
         if (j + 1 < T) issue_tile(Kn, Vn, kt0 + j + 1);
-        const bool prev = j >= 1 && active(kt0 + j - 1);
-        const bool cur = j < T && active(kt0 + j);
+        const bool prev = j >= 1 && active(j - 1);
+        const bool cur = j < T && active(j);
         if (!GB) {
           if (prev) pv(Vp);
           if (cur) {
             scores(Kc);
             __builtin_amdgcn_sched_barrier(0);
-            mask(kt0 + j);
+            mask(j);
             softmax(std::true_type{});
           }
         } else {
           if (prev) {
-            mask(kt0 + j - 1);
+            mask(j - 1);
             softmax(std::false_type{});
             // the softmax stays pure vector work: an MFMA issued among it would stall the
             // rest of it while the other group's MFMAs hold the matrix core
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_kernel(FwdArgs a) {
         __syncthreads();
       };
       // K slot j mod 2, V slot j mod 4: unrolled by four so every buffer is a fixed address
-      for (int64_t j = 0;; j += 4) {
+      for (int j = 0;; j += 4) {
         interval(j, sK0, sV3, sK1, sV1);
         if (j + 1 > T) break;
         interval(j + 1, sK1, sV0, sK0, sV2);
