@@ -597,8 +597,8 @@ def counter_summary(d, out=None, kernel=None):
     if out and kernel is None:
         rec = {"kernel": "ba::fwd_kernel<128>", "workload": "llama2_7b_s32k_ring8",
                "kernel_source_sha": _src_sha(FWD_SRC), "dispatches": len(rows),
-               "command": f"rocprofv3 --pmc {COUNTERS} -d {d} -o busy -- python -u bench.py --steps 1 "
-                          "--warmup 0 --no-cpu-baseline --no-side-measurements --no-backward",
+               "command": f"rocprofv3 --pmc {COUNTERS} -d {d} -o busy -- python -u bench.py --steps 2 "
+                          "--warmup 3 --no-cpu-baseline --no-side-measurements --no-backward",
                **{k: round(v, 4) for k, v in avg.items()}}
         with open(out, "w") as f:
             json.dump(rec, f, indent=1)
@@ -935,11 +935,6 @@ def main():
                 "counters": _counters("fwd_kernel_d128", r["src"], w.name),
                 "kernel": r["kernel"], "avg_launch_ms": round(avg_launch_ms, 4),
                 "launches_per_step": r["launches_per_step"]}
-    clk = (roofline["counters"] or {}).get("engine_clock_ghz")
-    if clk:
-        # the same work against the MFMA peak at the engine clock the profiled run measured for
-        # this kernel (cycles over dispatch time), not at the 2.4 GHz peak clock
-        roofline["frac_at_profiled_clock"] = round(achieved / (256 * 4096 * clk * 1e-3), 4)
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
