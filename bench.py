@@ -72,14 +72,19 @@ def run_ring_forward(w, steps, warmup):
     n = len(order)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
 
+    # each row's final bf16 output is stored by its last reaching step (ring.final_store_steps)
+    from long_context_exact_blockattn_amd.ring import final_store_steps
+    store = final_store_steps(order)
+
     def step(events=None):
         for t, c in enumerate(order):
             c0, c1 = bounds[c]
             if events is not None:
                 events[t].record()
+            mode = _lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE
             _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
-                               mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
-                               o_final=out if t == n - 1 else None, k_pos0=c0)
+                               mode=mode | _lib.BA_FINAL_REACHED_ONLY if store[t] else mode,
+                               o_final=out if store[t] else None, k_pos0=c0)
         if events is not None:
             events[n].record()
 
@@ -309,15 +314,18 @@ def run_training(w, steps, warmup, tensors=None, one_shot=True):
         bounds = chunk_bounds(w.seqlen, w.n_chunks)
         o_acc = torch.empty(b, s, hq, d, device=dev)
         n = len(order)
+        from long_context_exact_blockattn_amd.ring import final_store_steps
+        store = final_store_steps(order)
 
         def fwd(ev=None):
             for t, c in enumerate(order):
                 c0, c1 = bounds[c]
                 if ev is not None:
                     ev[t].record()
+                mode = _lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE
                 _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
-                                   mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
-                                   o_final=o if t == n - 1 else None, k_pos0=c0)
+                                   mode=mode | _lib.BA_FINAL_REACHED_ONLY if store[t] else mode,
+                                   o_final=o if store[t] else None, k_pos0=c0)
             if ev is not None:
                 ev[n].record()
 

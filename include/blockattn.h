@@ -69,7 +69,14 @@ typedef enum { BA_F32 = 0, BA_BF16 = 1 } ba_dtype;
 
 typedef enum {
   BA_OVERWRITE = 0,  /* (o, lse) := this chunk's partial pair, for EVERY query row */
-  BA_ACCUMULATE = 1  /* (o, lse) := merge((o, lse), partial); rows the chunk cannot reach are untouched */
+  BA_ACCUMULATE = 1, /* (o, lse) := merge((o, lse), partial); rows the chunk cannot reach are untouched */
+  /* Flag OR-ed into either mode of blockattn_fwd: with o_final, store the final
+   * output only for the query tiles the chunk reaches and leave the rows of the
+   * others untouched (no conversion of them from o).  For a causal ring whose
+   * caller passes o_final on each step that is the last one to reach some rows
+   * (the step's chunk precedes every later step's chunk), every row's final
+   * output is stored by that step. */
+  BA_FINAL_REACHED_ONLY = 4
 } ba_mode;
 
 typedef enum {
@@ -119,7 +126,9 @@ typedef struct {
  *   lse      [B,Hq,Sq] fp32, same in/out role as o.
  *   o_final  optional (NULL): bf16 [B,Sq,Hq,D] receives the normalised output of
  *            EVERY row after this step (rows the chunk cannot reach are converted
- *            from o), so the last ring step also produces the final result.
+ *            from o), so the last ring step also produces the final result; with
+ *            BA_FINAL_REACHED_ONLY in mode, only the rows of the query tiles the
+ *            chunk reaches.
  * Defined by the Ring Attention summary (Summary): blockwise attention of a
  * resident query block, combinable in any block order. */
 int blockattn_fwd(const ba_desc* desc, const void* q, const void* k, const void* v,

@@ -24,6 +24,7 @@ BA_ERR_WORKSPACE = 9
 NOALLOC_MAX_ROWS = 1 << 23  # BLOCKATTN_NOALLOC_MAX_ROWS
 BA_F32, BA_BF16 = 0, 1
 BA_OVERWRITE, BA_ACCUMULATE = 0, 1
+BA_FINAL_REACHED_ONLY = 4  # flag OR-ed into the forward mode
 BA_BWD_COMPUTE_DELTA, BA_BWD_FINALIZE_DQ = 1, 2
 
 

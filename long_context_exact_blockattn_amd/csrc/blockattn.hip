@@ -82,6 +82,8 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   if (r) return r;
   if (!std::isfinite(d->scale)) return BA_ERR_SHAPE;
   if (s2 && (r = check_s2(d, s2))) return r;
+  const bool final_reached_only = (mode & BA_FINAL_REACHED_ONLY) != 0;
+  mode &= ~(int32_t)BA_FINAL_REACHED_ONLY;
   if (mode != BA_OVERWRITE && mode != BA_ACCUMULATE) return BA_ERR_MODE;
   if (o_dtype != BA_F32 && o_dtype != BA_BF16) return BA_ERR_UNSUPPORTED;
   if (mode == BA_ACCUMULATE && o_dtype != BA_F32) return BA_ERR_MODE;
@@ -121,7 +123,7 @@ int fwd_impl(const ba_desc* d, const ba_s2_desc* s2, const void* q, const void* 
   a.n_items = (int64_t)d->batch * d->heads_q * a.n_ranks;
   a.hx = interleave_heads((int64_t)d->batch * d->heads_q, a.n_ranks, kFwdSlotsPerXcd);
   if (a.n_items > 0x7fffffffLL) return BA_ERR_SHAPE;
-  if (o_final && skip_qt > 0) {
+  if (o_final && skip_qt > 0 && !final_reached_only) {
     StoreArgs st;
     st.o_acc = (const float*)o;
     st.o_final = (bf16*)o_final;

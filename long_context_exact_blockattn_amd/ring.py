@@ -17,14 +17,41 @@ def _bounds(seqlen_k, n_chunks):
     return [(i * c, min((i + 1) * c, seqlen_k)) for i in range(n_chunks) if i * c < seqlen_k]
 
 
+def final_store_steps(order, causal=True):
+    """Which ring positions store the final bf16 output, and for which rows.
+
+    Under the causal mask, chunk c reaches exactly the rows from its own start on, so a row's
+    last reaching step is the last position whose chunk is at or before the row's block: the
+    rows of blocks [c_t, min of the later chunks) are final after position t.  Those positions
+    (each one whose chunk precedes every later chunk, always the last) pass o_final with
+    BA_FINAL_REACHED_ONLY and store every row they reach, so each row's final output is stored
+    by its last reaching step and no step converts the rows it cannot reach.  Without the mask
+    every step reaches every row: only the last one stores.
+    Returns one bool per position.
+    """
+    n = len(order)
+    if not causal:
+        return [t == n - 1 for t in range(n)]
+    flags, later_min = [False] * n, n
+    for t in range(n - 1, -1, -1):
+        flags[t] = order[t] < later_min
+        later_min = min(later_min, order[t])
+    return flags
+
+
+def _step_mode(t, store, causal):
+    mode = _lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE
+    return mode | _lib.BA_FINAL_REACHED_ONLY if (store and causal) else mode
+
+
 def ring_forward(q, k, v, n_chunks, order=None, *, causal=True, scale=None, o_acc=None, lse=None,
                  out=None, stream=None):
     """Forward over `n_chunks` key/value chunks visited in `order`.
 
     Returns (out bf16 [B,S,Hq,D], lse fp32 [B,Hq,S], o_acc fp32 [B,S,Hq,D]).
     Step 0 overwrites the running pair (rows its chunk cannot reach become the
-    empty pair (0, -inf)); later steps accumulate; the last one also stores the
-    final bf16 output for every row.
+    empty pair (0, -inf)); later steps accumulate; the final bf16 output of each
+    row is stored by its last reaching step (final_store_steps).
     """
     bounds = _bounds(k.shape[1], n_chunks)
     order = list(range(len(bounds))) if order is None else list(order)
@@ -37,11 +64,11 @@ def ring_forward(q, k, v, n_chunks, order=None, *, causal=True, scale=None, o_ac
         lse = torch.empty(b, hq, s, device=q.device, dtype=torch.float32)
     if out is None:
         out = torch.empty(b, s, hq, d, device=q.device, dtype=torch.bfloat16)
+    store = final_store_steps(order, causal)
     for t, c in enumerate(order):
         c0, c1 = bounds[c]
-        _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse,
-                           mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
-                           o_final=out if t == len(order) - 1 else None,
+        _lib.blockattn_fwd(q, k[:, c0:c1], v[:, c0:c1], o_acc, lse, mode=_step_mode(t, store[t], causal),
+                           o_final=out if store[t] else None,
                            k_pos0=c0, causal=causal, scale=scale, stream=stream)
     return out, lse, o_acc
 
@@ -97,6 +124,7 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
             vbuf[slot][:, : c1 - c0].copy_(v[:, c0:c1], non_blocking=True)
             copied[slot].record(side)
 
+    store = final_store_steps(order, causal)
     copy(0)
     for t in range(len(order)):
         slot = t % 2
@@ -105,8 +133,7 @@ def ring_forward_staged(q, k, v, n_chunks, order=None, *, causal=True, scale=Non
             copy(t + 1)
         main.wait_event(copied[slot])
         _lib.blockattn_fwd(q, kbuf[slot][:, : c1 - c0], vbuf[slot][:, : c1 - c0], o_acc, lse,
-                           mode=_lib.BA_OVERWRITE if t == 0 else _lib.BA_ACCUMULATE,
-                           o_final=out if t == len(order) - 1 else None,
+                           mode=_step_mode(t, store[t], causal), o_final=out if store[t] else None,
                            k_pos0=c0, causal=causal, scale=scale, stream=main)
         computed[slot].record(main)
     # the side stream read k and v and wrote the staging buffers: none of them may be

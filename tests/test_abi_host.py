@@ -70,7 +70,8 @@ def test_fwd_validation_codes(lib):
     assert _fwd(lib, _desc(), lse=FAKE + 2) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), of=FAKE + 8) == _lib.BA_ERR_ALIGN
     assert _fwd(lib, _desc(), q=0) == _lib.BA_ERR_NULL
-    assert _fwd(lib, _desc(), mode=5) == _lib.BA_ERR_MODE
+    assert _fwd(lib, _desc(), mode=2) == _lib.BA_ERR_MODE
+    assert _fwd(lib, _desc(), mode=6) == _lib.BA_ERR_MODE  # a mode flag does not make 2 a mode
     assert _fwd(lib, _desc(), odt=_lib.BA_BF16, mode=_lib.BA_ACCUMULATE) == _lib.BA_ERR_MODE
     assert _fwd(lib, _desc(), odt=7) == _lib.BA_ERR_UNSUPPORTED
     assert _fwd(lib, _desc(causal=2)) == _lib.BA_ERR_SHAPE
@@ -355,3 +356,27 @@ def test_noalloc_rejects_problems_beyond_its_scratch_buffer(lib):
     assert lib.blockattn_bwd_noalloc(None, *([P(FAKE)] * 9), _lib.BA_BF16, None, 0, None) == _lib.BA_ERR_NULL
     d = _desc(Sq=-1)
     assert lib.blockattn_bwd_noalloc(ctypes.byref(d), *([P(FAKE)] * 9), _lib.BA_BF16, None, 0, None) == _lib.BA_ERR_SHAPE
+
+
+def test_final_store_steps_cover_every_rows_last_reaching_step():
+    """Under the causal mask chunk c reaches the row blocks c, c+1, ...; the positions that store
+    the final output (ring.final_store_steps) must include every block's last reaching position,
+    and a stored value is final only there: brute force over all orders of up to 6 chunks and
+    random orders of 16."""
+    import itertools
+    import random
+    from long_context_exact_blockattn_amd.ring import final_store_steps
+    orders = [list(p) for n in range(1, 7) for p in itertools.permutations(range(n))]
+    rnd = random.Random(0)
+    orders += [rnd.sample(range(16), 16) for _ in range(200)]
+    for order in orders:
+        n = len(order)
+        store = final_store_steps(order)
+        assert store[-1]
+        for blk in range(n):
+            reaching = [t for t, c in enumerate(order) if c <= blk]
+            writes = [t for t in reaching if store[t]]  # stores touch only rows their chunk reaches
+            assert writes and writes[-1] == reaching[-1], (order, blk)
+        assert final_store_steps(order, causal=False) == [t == n - 1 for t in range(n)]
+    # the headline order stores at three positions: chunks 0 (block 0), 1 (blocks 1-6), 7 (block 7)
+    assert final_store_steps([2, 4, 3, 6, 5, 0, 1, 7]) == [False] * 5 + [True] * 3

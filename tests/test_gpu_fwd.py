@@ -150,6 +150,50 @@ def test_accumulate_late_chunk_ragged(B, S, k0):
     _check_pair(f"late chunk B={B} S={S} k0={k0}", o, lse, o_ref, l_ref, fin)
 
 
+@pytest.mark.parametrize("B,S,k0", [(1, 1000, 130), (2, 700, 390), (1, 2048, 1024)])
+def test_final_reached_only_leaves_unreached_tiles(B, S, k0):
+    # BA_FINAL_REACHED_ONLY: the final bf16 output is stored for the query tiles the chunk
+    # reaches (256 rows each, so the rows of the tile holding k0 before k0 too) and the rows of
+    # the tiles wholly before the chunk keep what the caller stored there
+    H, D, BM = 2, 128, 256
+    q, k, v = make_inputs(B, S, H, H, D, seed=23 + k0)
+    qd, kd, vd = _to_dev(q, k, v)
+    first = S // 2
+    o = torch.empty((B, S, H, D), device=dev())
+    lse = torch.empty((B, H, S), device=dev())
+    ba.blockattn_fwd(qd, kd[:, :first], vd[:, :first], o, lse)
+    fin = torch.full((B, S, H, D), 7.0, device=dev(), dtype=torch.bfloat16)
+    n2 = min(S - first, 64)
+    ba.blockattn_fwd(qd, kd[:, first:first + n2], vd[:, first:first + n2], o, lse,
+                     mode=ba.BA_ACCUMULATE | ba.BA_FINAL_REACHED_ONLY, k_pos0=k0, o_final=fin)
+    torch.cuda.synchronize()
+    lo = (k0 // BM) * BM  # first row of the first reached tile
+    assert torch.all(fin[:, :lo] == 7.0)
+    assert torch.equal(fin[:, lo:], o[:, lo:].to(torch.bfloat16))
+    o_a, l_a = attention_forward(f64(q), f64(k[:, :first]), f64(v[:, :first]))
+    o_b, l_b = attention_forward(f64(q), f64(k[:, first:first + n2]), f64(v[:, first:first + n2]), k_pos0=k0)
+    o_ref, l_ref = lse_merge(o_a, l_a, o_b, l_b)
+    _check_pair(f"reached-only B={B} S={S} k0={k0}", o, lse, o_ref, l_ref)
+
+
+@pytest.mark.parametrize("n_chunks,S,causal", [(8, 2048, True), (5, 1000, True), (4, 1024, False)])
+def test_ring_final_store_steps_store_every_row(n_chunks, S, causal):
+    # the ring stores each row's final output at its last reaching step only (no conversion of
+    # unreached rows); every row of the result must be the rounding of the final running output
+    H, D = 2, 128
+    q, k, v = make_inputs(1, S, H, H, D, seed=31 + n_chunks)
+    qd, kd, vd = _to_dev(q, k, v)
+    o_ref, l_ref = attention_forward(f64(q), f64(k), f64(v), causal=causal)
+    for seed in range(4):
+        order = chunk_order(n_chunks, seed=seed)
+        out = torch.full((1, S, H, D), float("nan"), device=dev(), dtype=torch.bfloat16)
+        out, lse, o_acc = ba.ring_forward(qd, kd, vd, n_chunks, order, causal=causal, out=out)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any()
+        assert torch.equal(out, o_acc.to(torch.bfloat16))
+        _check_pair(f"final store n={n_chunks} S={S} order={order}", o_acc, lse, o_ref, l_ref, out)
+
+
 @pytest.mark.parametrize("S,D", [(1000, 128), (333, 64)])
 def test_ring_accumulate_into_strided_outputs(S, D):
     # a causal ring whose running output, LSE-paired bf16 result and the interleaved slices
